@@ -1,0 +1,200 @@
+"""Seeded synthetic inputs for the IKBO Linear Compression Embedding forward.
+
+This module is the one piece of code shared by the CPU oracle's tests and the
+HIP path's tests and bench: it draws the input tensors and nothing else. It
+holds none of the operator's arithmetic (no products, no sums, no broadcast).
+
+Workload shapes.  The pages give the shape facts only: a request of 1024
+candidates against about 15 users, a 70:1 ratio ("Deep Dive: Linear
+Compression", stage 1, IKBO recsys blog), and an operating envelope of batch
+256-4096 with ratios 10:1 to 10000:1 (zubnet summary, practical advice
+paragraph).  K, M and D are never printed, so the five configurations below fix
+them; they stand in for the non-public default benchmark and production models.
+
+Draw recipe (a reading; the pages give no seeds or generator):
+  * ``numpy.random.default_rng(seed)`` (PCG64), seed = configuration index;
+  * draw order U, C, W_u, W_c as float32 standard normals, then the map (only
+    for the unsorted configuration) with ``integers(0, B_u, B_c)``;
+  * weights are scaled by ``w_std`` = 1/sqrt(K_u + K_c) (fan-in reading of
+    "N(0, 1/sqrt(K))": the value is the standard deviation);
+  * bf16 configurations round every drawn float32 to bfloat16 with
+    round-to-nearest-even; the same bytes feed both the oracle and the GPU;
+  * sorted maps give user ``i`` a contiguous run of candidates; when B_c is not
+    a multiple of B_u the first ``B_c mod B_u`` users get one extra candidate.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+DTYPE_BF16 = "bf16"
+DTYPE_F32 = "f32"
+
+
+@dataclasses.dataclass(frozen=True)
+class LceConfig:
+    """Shape and distribution of one synthetic LCE workload."""
+
+    name: str
+    B_u: int
+    B_c: int
+    K_u: int
+    K_c: int
+    M: int
+    D: int
+    dtype: str          # "bf16" or "f32": U, C, W_u, W_c and Y
+    map_kind: str       # "sorted", "random" or "explicit"
+    seed: int
+    explicit_map: Optional[tuple] = None
+
+    @property
+    def w_std(self) -> float:
+        return 1.0 / float(np.sqrt(self.K_u + self.K_c))
+
+    @property
+    def elt_size(self) -> int:
+        return 2 if self.dtype == DTYPE_BF16 else 4
+
+    def with_batch(self, B_u: int, B_c: int, name: Optional[str] = None) -> "LceConfig":
+        return dataclasses.replace(self, B_u=B_u, B_c=B_c, explicit_map=None,
+                                   map_kind="sorted" if self.map_kind == "explicit" else self.map_kind,
+                                   name=name or f"{self.name}-Bu{B_u}-Bc{B_c}")
+
+
+CONFIGS = [
+    LceConfig("tiny", 2, 8, 13, 11, 8, 16, DTYPE_F32, "explicit", 0,
+              explicit_map=(0, 0, 0, 0, 1, 1, 1, 1)),
+    LceConfig("default-70to1", 15, 1024, 301, 197, 96, 160, DTYPE_BF16, "sorted", 1),
+    LceConfig("small-10to1", 26, 256, 301, 197, 96, 160, DTYPE_BF16, "sorted", 2),
+    LceConfig("large-unsorted", 59, 4096, 301, 197, 96, 160, DTYPE_BF16, "random", 3),
+    LceConfig("extreme-10000to1", 2, 20000, 509, 251, 128, 128, DTYPE_BF16, "sorted", 4),
+]
+CONFIG_BY_NAME = {c.name: c for c in CONFIGS}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return the bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    # No overflow for any non-NaN pattern: the largest finite magnitude plus 0x8000
+    # stays below 2**32, and infinities keep their exponent.
+    r = (u >> 16) & 1
+    r += 0x7FFF
+    r += u
+    r >>= 16
+    out = r.astype(np.uint16)
+    nan = x != x
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 exactly."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+def sorted_map(B_u: int, B_c: int) -> np.ndarray:
+    """Contiguous runs: user i owns one block of ``np.array_split(range(B_c), B_u)``."""
+    m = np.empty(B_c, dtype=np.int32)
+    for u, idx in enumerate(np.array_split(np.arange(B_c), B_u)):
+        m[idx] = u
+    return m
+
+
+def default_map(cfg: LceConfig) -> np.ndarray:
+    """The map ``make_inputs(cfg)`` produces (the random one needs the full draw)."""
+    if cfg.map_kind == "explicit":
+        return np.asarray(cfg.explicit_map, dtype=np.int32)
+    if cfg.map_kind == "random":
+        return make_inputs(cfg).map
+    return sorted_map(cfg.B_u, cfg.B_c)
+
+
+@dataclasses.dataclass
+class LceInputs:
+    """One seeded draw. Floating tensors are uint16 bf16 bit patterns or float32."""
+
+    cfg: LceConfig
+    U: np.ndarray       # [B_u, K_u, D]
+    C: np.ndarray       # [B_c, K_c, D]
+    W_u: np.ndarray     # [M, K_u]
+    W_c: np.ndarray     # [M, K_c]
+    map: np.ndarray     # [B_c] int32
+
+    def as_f32(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        return bf16_bits_to_f32(a) if a.dtype == np.uint16 else a
+
+
+def _round_bf16_fast(x: np.ndarray) -> np.ndarray:
+    """Same result as ``f32_to_bf16_bits`` for every non-NaN value (drawn data has no
+    NaN), computed with torch's multi-threaded cast; numpy fallback otherwise."""
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        return f32_to_bf16_bits(x)
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    return _round_bf16_fast(x) if dtype == DTYPE_BF16 else np.ascontiguousarray(x, dtype=np.float32)
+
+
+def make_inputs(cfg: LceConfig, seed: Optional[int] = None) -> LceInputs:
+    """Draw the inputs of ``cfg`` with the recipe in the module docstring."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    U = rng.standard_normal((cfg.B_u, cfg.K_u, cfg.D), dtype=np.float32)
+    U = _store(U, cfg.dtype)
+    C = rng.standard_normal((cfg.B_c, cfg.K_c, cfg.D), dtype=np.float32)
+    C = _store(C, cfg.dtype)
+    w = np.float32(cfg.w_std)
+    W_u = _store(rng.standard_normal((cfg.M, cfg.K_u), dtype=np.float32) * w, cfg.dtype)
+    W_c = _store(rng.standard_normal((cfg.M, cfg.K_c), dtype=np.float32) * w, cfg.dtype)
+    if cfg.map_kind == "explicit":
+        mp = np.asarray(cfg.explicit_map, dtype=np.int32)
+    elif cfg.map_kind == "random":
+        mp = rng.integers(0, cfg.B_u, cfg.B_c).astype(np.int32)
+    else:
+        mp = sorted_map(cfg.B_u, cfg.B_c)
+    return LceInputs(cfg, U, C, W_u, W_c, mp)
+
+
+def make_integer_inputs(cfg: LceConfig, seed: int = 12345) -> LceInputs:
+    """Inputs and weights drawn from {-1, 0, 1}: every partial sum is a small integer,
+    exact in fp32, so any correct summation order yields identical bits."""
+    rng = np.random.default_rng(seed)
+
+    def draw(shape):
+        return _store(rng.integers(-1, 2, size=shape).astype(np.float32), cfg.dtype)
+
+    U = draw((cfg.B_u, cfg.K_u, cfg.D))
+    C = draw((cfg.B_c, cfg.K_c, cfg.D))
+    W_u = draw((cfg.M, cfg.K_u))
+    W_c = draw((cfg.M, cfg.K_c))
+    if cfg.map_kind == "explicit":
+        mp = np.asarray(cfg.explicit_map, dtype=np.int32)
+    elif cfg.map_kind == "random":
+        mp = rng.integers(0, cfg.B_u, cfg.B_c).astype(np.int32)
+    else:
+        mp = sorted_map(cfg.B_u, cfg.B_c)
+    return LceInputs(cfg, U, C, W_u, W_c, mp)
+
+
+def make_tag_inputs(cfg: LceConfig, mp: Optional[np.ndarray] = None) -> LceInputs:
+    """Gather tag: U[u,0,:] = u+1, W_u[:,0] = 1, all else zero, C = 0.
+    The operator then yields Y[b,m,d] = map[b] + 1 (exact up to 256 in bf16)."""
+    U = np.zeros((cfg.B_u, cfg.K_u, cfg.D), dtype=np.float32)
+    U[:, 0, :] = (np.arange(cfg.B_u, dtype=np.float32) + 1.0)[:, None]
+    C = np.zeros((cfg.B_c, cfg.K_c, cfg.D), dtype=np.float32)
+    W_u = np.zeros((cfg.M, cfg.K_u), dtype=np.float32)
+    W_u[:, 0] = 1.0
+    W_c = np.zeros((cfg.M, cfg.K_c), dtype=np.float32)
+    if mp is None:
+        mp = default_map(cfg)
+    return LceInputs(cfg, _store(U, cfg.dtype), _store(C, cfg.dtype), _store(W_u, cfg.dtype),
+                     _store(W_c, cfg.dtype), np.asarray(mp, dtype=np.int32))

@@ -1,0 +1,126 @@
+"""CPU oracle for the IKBO Linear Compression Embedding forward.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product package never imports this
+module, and this module imports nothing from the product package.
+
+The arithmetic lives in ``ikbo_oracle.c`` (plain C, fp64): it materialises the
+broadcast ``X_b = [U[map[b]] ; C[b]]`` and computes ``Y[b] = [W_u | W_c] . X_b``
+(IKBO recsys blog, "Deep Dive: Linear Compression": the baseline batched matmul
+and the stage-1 decomposition it equals by linearity).  This wrapper only
+marshals numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ikbo_oracle.c")
+_LIB = os.path.join(_HERE, "libikbo_oracle.so")
+
+ORACLE_BF16 = 0
+ORACLE_F32 = 1
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+           "-std=c11", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.ikbo_oracle_lce_f64.restype = ctypes.c_int
+        lib.ikbo_oracle_lce_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
+        lib.ikbo_oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().ikbo_oracle_max_threads())
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def lce_f64(U: np.ndarray, C: np.ndarray, mp: np.ndarray, W_u: np.ndarray, W_c: np.ndarray,
+            rows: Optional[Sequence[int]] = None, threads: int = 0) -> np.ndarray:
+    """Y[b] = W_u . U[map[b]] + W_c . C[b] in fp64, via the materialised form.
+
+    Floating inputs are either all ``uint16`` bfloat16 bit patterns or all
+    ``float32``.  ``rows`` selects candidates (default: all); the result has
+    shape [len(rows), M, D] (or [B_c, M, D]).
+    """
+    dt = U.dtype
+    if not all(a.dtype == dt for a in (C, W_u, W_c)):
+        raise TypeError("U, C, W_u, W_c must share one dtype")
+    if dt == np.uint16:
+        code = ORACLE_BF16
+    elif dt == np.float32:
+        code = ORACLE_F32
+    else:
+        raise TypeError(f"unsupported dtype {dt}")
+    B_u, K_u, D = U.shape
+    B_c, K_c, D2 = C.shape
+    M, K_u2 = W_u.shape
+    M2, K_c2 = W_c.shape
+    if (D, K_u, K_c, M) != (D2, K_u2, K_c2, M2) or mp.shape != (B_c,):
+        raise ValueError("inconsistent shapes")
+    U = np.ascontiguousarray(U)
+    C = np.ascontiguousarray(C)
+    W_u = np.ascontiguousarray(W_u)
+    W_c = np.ascontiguousarray(W_c)
+    mp = np.ascontiguousarray(mp, dtype=np.int32)
+    if rows is None:
+        n = B_c
+        rows_arr = None
+        rows_ptr = None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = rows_arr.shape[0]
+        rows_ptr = rows_arr.ctypes.data
+    Y = np.empty((n, M, D), dtype=np.float64)
+    st = _load().ikbo_oracle_lce_f64(
+        U.ctypes.data, C.ctypes.data, mp.ctypes.data, W_u.ctypes.data, W_c.ctypes.data,
+        Y.ctypes.data, B_u, B_c, K_u, K_c, M, D, code, rows_ptr, n, int(threads))
+    if st != 0:
+        raise OracleError(f"oracle returned {st}")
+    return Y
+
+
+def tolerance_violations(Y_gpu: np.ndarray, Y_ref: np.ndarray, atol: float = 1e-3,
+                         rtol: float = 1.6e-2):
+    """Count elements with |Y_gpu - Y_ref| > atol + rtol*|Y_ref| (bf16 inputs, fp32
+    accumulation: the acceptance bound of the IKBO LCE parity contract).  NaNs
+    count as violations unless both sides are NaN.  Returns (count, max_excess)."""
+    Y_gpu = np.asarray(Y_gpu, dtype=np.float64)
+    err = np.abs(Y_gpu - Y_ref)
+    bound = atol + rtol * np.abs(Y_ref)
+    both_nan = np.isnan(Y_gpu) & np.isnan(Y_ref)
+    same_inf = np.isinf(Y_gpu) & (Y_gpu == Y_ref)
+    bad = ~(err <= bound) & ~both_nan & ~same_inf
+    excess = np.where(bad, err - bound, 0.0)
+    ex = float(np.nanmax(excess)) if excess.size else 0.0
+    return int(bad.sum()), ex
