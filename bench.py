@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Throughput of the IKBO Linear Compression Embedding forward on one MI355X.
+
+One step = one forward Y[b] = W_u.U[map[b]] + W_c.C[b] over one batch of seeded
+synthetic inputs already resident in HBM (default workload: B_u = 15 users,
+B_c = 1024 candidates, sorted map, K_u = 301, K_c = 197, M = 96, D = 160, bf16).
+Input/output sets are rotated through >= 1 GB of distinct buffers so the
+256 MB Infinity Cache cannot serve repeated reads.
+
+Prints one JSON line: the value is the algorithmic HBM throughput (bytes the
+method must move: U + C + W_u + W_c + map + Y, once each) per second, with the
+time per forward, TFLOP/s, the roofline fraction of the (single) forward
+kernel, and the CPU oracle timed on this host as a reported baseline.
+
+    python bench.py [--steps K] [--warmup W] [--variant S4] [--config default-70to1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "IKBO-LCE fwd µs + TFLOP/s & HBM GB/s at B_c=1024, 70:1; % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+KERNEL_SOURCES = ["broadcast_gemm_amd/csrc/lce_fused.hip", "broadcast_gemm_amd/csrc/lce_tile.h",
+                  "broadcast_gemm_amd/csrc/lce_device.h", "broadcast_gemm_amd/csrc/lce_kernels.hip",
+                  "broadcast_gemm_amd/csrc/ikbo_api.cpp"]
+
+
+def algorithmic_bytes(cfg) -> int:
+    e = cfg.elt_size
+    return (e * (cfg.B_u * cfg.K_u * cfg.D + cfg.B_c * cfg.K_c * cfg.D + cfg.M * cfg.K_u + cfg.M * cfg.K_c
+                 + cfg.B_c * cfg.M * cfg.D) + 4 * cfg.B_c)
+
+
+def algorithmic_flops(cfg) -> int:
+    return 2 * cfg.M * cfg.D * (cfg.B_u * cfg.K_u + cfg.B_c * cfg.K_c)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, variant: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, scaled by
+    the same counters on a copy kernel; null if the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{variant}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, x, min_seconds: float, max_reps: int):
+    """The oracle as it stands, on the full workload, repeated until min_seconds."""
+    import oracle
+    threads = oracle.max_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.lce_f64(x.U, x.C, x.map, x.W_u, x.W_c, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= max_reps:
+            break
+    gbs = algorithmic_bytes(cfg) * reps / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"full {cfg.name} workload x {reps} (fp64, materialised broadcast, naive product); "
+                      f"{el:.1f} s wall", "seconds_per_forward": round(el / reps, 4)}
+
+
+def run_copy(args) -> int:
+    """Plain device copy of known size (calibrates FETCH_SIZE/WRITE_SIZE counters)."""
+    import torch
+    n = args.copy_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": args.steps}), flush=True)
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="default-70to1")
+    ap.add_argument("--variant", default="auto", choices=["auto", "S0", "S1", "S2", "S3", "S4"])
+    ap.add_argument("--rotate-mb", type=int, default=1100, help="total size of rotated buffer sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--mode", default="lce", choices=["lce", "copy"])
+    ap.add_argument("--copy-mib", type=int, default=256)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the IKBO LCE forward needs no collective, and "
+              f"--gpus {args.gpus} is not supported by this build.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    if args.mode == "copy":
+        return run_copy(args)
+
+    import broadcast_gemm_amd as bga
+    from broadcast_gemm_amd.inputs import CONFIG_BY_NAME, bf16_bits_to_f32, make_inputs
+
+    cfg = CONFIG_BY_NAME[args.config]
+    torch.cuda.set_device(0)
+    print(f"[bench] config={cfg.name} variant={args.variant} steps={args.steps} warmup={args.warmup}",
+          file=sys.stderr, flush=True)
+    x = make_inputs(cfg)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    base = [dev(a) for a in (x.U, x.C, x.map, x.W_u, x.W_c)]
+    tdt = base[0].dtype
+    set_bytes = sum(t.numel() * t.element_size() for t in base) + cfg.B_c * cfg.M * cfg.D * base[0].element_size()
+    n_sets = max(1, math.ceil(args.rotate_mb * 2**20 / set_bytes))
+    sets = []
+    for i in range(n_sets):
+        ins = base if i == 0 else [t.clone() for t in base]
+        Y = torch.empty((cfg.B_c, cfg.M, cfg.D), dtype=tdt, device="cuda")
+        sets.append(ins + [Y])
+    plan = bga.LcePlan(cfg.B_u, cfg.B_c, cfg.K_u, cfg.K_c, cfg.M, cfg.D, dtype=cfg.dtype, variant=args.variant)
+    info = plan.info()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(i):
+        U, C, mp, W_u, W_c, Y = sets[i % n_sets]
+        st = plan.forward_ptrs(U.data_ptr(), C.data_ptr(), mp.data_ptr(), W_u.data_ptr(), W_c.data_ptr(),
+                               Y.data_ptr(), cfg.B_u, cfg.B_c, sh)
+        if st != bga.IKBO_OK:
+            raise bga.IkboError(st, "ikbo_lce_forward")
+
+    for i in range(args.warmup):
+        step(i)
+    st = plan.check()
+    if st != bga.IKBO_OK:
+        raise bga.IkboError(st, "warmup device status")
+
+    K = args.steps
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev0[i].record(stream)
+        step(i)
+        ev1[i].record(stream)
+    torch.cuda.synchronize()
+    st = plan.check()
+    if st != bga.IKBO_OK:
+        raise bga.IkboError(st, "timed device status")
+    total_ms = ev0[0].elapsed_time(ev1[K - 1])
+    per_launch = [ev0[i].elapsed_time(ev1[i]) for i in range(K)]
+    ms_per_step = total_ms / K
+    launch_ms = sum(per_launch) / K
+    launch_sorted = sorted(per_launch)
+
+    # Warm (same buffers every launch) figure, labelled separately.
+    torch.cuda.synchronize()
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for i in range(K):
+        step(0)
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / K
+
+    # Parity of the last output of set 0 against the oracle on sampled candidates (untimed).
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = sorted(set([0, 1, cfg.B_c // 2, cfg.B_c - 1] + list(range(0, cfg.B_c, max(1, cfg.B_c // 16)))))
+        Y = sets[0][5]
+        if Y.dtype == torch.bfloat16:
+            Yn = bf16_bits_to_f32(Y.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+        else:
+            Yn = Y.cpu().numpy().astype(np.float64)
+        ref = oracle.lce_f64(x.U, x.C, x.map, x.W_u, x.W_c, rows=rows)
+        nbad, _ = oracle.tolerance_violations(Yn[rows], ref)
+        parity = {"rows_checked": len(rows), "violations": nbad}
+
+    nbytes = algorithmic_bytes(cfg)
+    flops = algorithmic_flops(cfg)
+    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B_u": cfg.B_u, "B_c": cfg.B_c, "K_u": cfg.K_u, "K_c": cfg.K_c,
+                   "M": cfg.M, "D": cfg.D, "map": cfg.map_kind, "variant": info["variant"],
+                   "rotating_sets": n_sets, "parallelism": "single GPU"},
+        "us_per_forward": round(ms_per_step * 1e3, 3),
+        "us_per_forward_p10_p50_p90": [round(launch_sorted[int(q * (K - 1))] * 1e3, 3) for q in (0.1, 0.5, 0.9)],
+        "us_per_forward_warm_same_buffers": round(warm_ms * 1e3, 3),
+        "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "mfma_frac_of_bf16_peak": round(flops / (launch_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "algorithmic_bytes": nbytes,
+        "algorithmic_flops": flops,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(cfg.name, info["variant"]),
+                     "kernel": "lce_fused_kernel" if info["variant"] == "S4" else "whole forward",
+                     "launch_us": round(launch_ms * 1e3, 3)},
+        "plan": info,
+        "parity": parity,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_seconds, 50)
+    plan.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,206 @@
+"""broadcast_gemm_amd -- IKBO Linear Compression Embedding forward for AMD MI355X.
+
+    Y[b] = W_u . U[map[b]] + W_c . C[b]
+
+Python binding of the C ABI in ``include/ikbo.h`` (``libikbo.so``).  This layer
+only marshals arguments: every step of the forward runs in the library's HIP
+kernels.  PyTorch supplies device memory and streams.  There is no CPU path:
+if the library is not built, every call raises.
+
+    plan = LcePlan(max_B_u, max_B_c, K_u, K_c, M, D, dtype="bf16", variant="S4")
+    Y = plan.forward(U, C, map, W_u, W_c)        # torch tensors on the GPU
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libikbo.so")
+
+IKBO_OK = 0
+IKBO_ERR_INVALID_ARG = -1
+IKBO_ERR_UNSUPPORTED = -2
+IKBO_ERR_HIP = -3
+IKBO_ERR_ALIGNMENT = -4
+IKBO_ERR_TIMEOUT = -5
+IKBO_ERR_MAP_RANGE = -6
+
+DTYPES = {"bf16": 0, "f32": 1}
+VARIANTS = {"auto": 0, "S0": 1, "S1": 2, "S2": 3, "S3": 4, "S4": 5}
+FLAG_DEBUG_DELAY_USER = 2
+FLAG_DEBUG_SKIP_USER = 4
+
+# Every symbol include/ikbo.h declares.
+EXPORTED = ("ikbo_lce_plan", "ikbo_lce_forward", "ikbo_lce_check", "ikbo_lce_plan_info",
+            "ikbo_lce_plan_set_spin_limit", "ikbo_lce_plan_destroy", "ikbo_status_str",
+            "ikbo_last_error_message")
+
+
+class IkboError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = f"{what}: " if what else ""
+        msg += f"{status_str(status)} ({status})"
+        if status == IKBO_ERR_HIP:
+            msg += f": {last_error_message()}"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libikbo.so with its prototypes; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m broadcast_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, ip, i, u32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_size_t
+        L.ikbo_lce_plan.argtypes = [ctypes.POINTER(vp), i, i, i, i, i, i, i, i, ctypes.c_uint]
+        L.ikbo_lce_plan.restype = ip
+        L.ikbo_lce_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+        L.ikbo_lce_forward.restype = ip
+        L.ikbo_lce_check.argtypes = [vp, vp]
+        L.ikbo_lce_check.restype = ip
+        L.ikbo_lce_plan_info.argtypes = [vp, ctypes.c_char_p, sz]
+        L.ikbo_lce_plan_info.restype = ip
+        L.ikbo_lce_plan_set_spin_limit.argtypes = [vp, u32]
+        L.ikbo_lce_plan_set_spin_limit.restype = ip
+        L.ikbo_lce_plan_destroy.argtypes = [vp]
+        L.ikbo_lce_plan_destroy.restype = ip
+        L.ikbo_status_str.argtypes = [ip]
+        L.ikbo_status_str.restype = ctypes.c_char_p
+        L.ikbo_last_error_message.argtypes = []
+        L.ikbo_last_error_message.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().ikbo_status_str(int(status)).decode()
+
+
+def last_error_message() -> str:
+    return lib().ikbo_last_error_message().decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class LcePlan:
+    """A plan for one shape range; owns the device workspace (see ``ikbo_lce_plan``)."""
+
+    def __init__(self, max_B_u: int, max_B_c: int, K_u: int, K_c: int, M: int, D: int,
+                 dtype: str = "bf16", variant: str = "auto", flags: int = 0):
+        self.dims = (K_u, K_c, M, D)
+        self.max_B_u, self.max_B_c = max_B_u, max_B_c
+        self.dtype = dtype
+        self.variant = variant
+        h = ctypes.c_void_p()
+        st = lib().ikbo_lce_plan(ctypes.byref(h), max_B_u, max_B_c, K_u, K_c, M, D, DTYPES[dtype],
+                                 VARIANTS[variant], flags)
+        if st != IKBO_OK:
+            raise IkboError(st, "ikbo_lce_plan")
+        self._h = h
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise ValueError("plan destroyed")
+        return self._h
+
+    def info(self) -> dict:
+        buf = ctypes.create_string_buffer(2048)
+        n = lib().ikbo_lce_plan_info(self.handle, buf, len(buf))
+        if n < 0:
+            raise IkboError(n, "ikbo_lce_plan_info")
+        return json.loads(buf.value.decode())
+
+    def set_spin_limit(self, polls: int) -> None:
+        st = lib().ikbo_lce_plan_set_spin_limit(self.handle, polls)
+        if st != IKBO_OK:
+            raise IkboError(st, "ikbo_lce_plan_set_spin_limit")
+
+    def forward_ptrs(self, U: int, C: int, mp: int, W_u: int, W_c: int, Y: int, B_u: int, B_c: int,
+                     stream: Optional[int] = None) -> int:
+        """Raw C-ABI call on device pointers; returns the status code."""
+        K_u, K_c, M, D = self.dims
+        return lib().ikbo_lce_forward(self.handle, U, C, mp, W_u, W_c, Y, B_u, B_c, K_u, K_c, M, D, stream)
+
+    def forward(self, U, C, mp, W_u, W_c, out=None, stream=None):
+        """Y = W_u . U[map] + W_c . C on the current (or given) stream; returns Y."""
+        torch = _torch()
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        for name, t in (("U", U), ("C", C), ("W_u", W_u), ("W_c", W_c)):
+            if t.dtype != tdt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {tdt} tensor on the GPU")
+        if mp.dtype != torch.int32:
+            mp = mp.to(torch.int32)
+        mp = mp.contiguous()
+        B_u, K_u, D = U.shape
+        B_c = C.shape[0]
+        M = W_u.shape[0]
+        if out is None:
+            out = torch.empty((B_c, M, D), dtype=tdt, device=C.device)
+        elif out.dtype != tdt or not out.is_contiguous() or tuple(out.shape) != (B_c, M, D):
+            raise ValueError("out must be a contiguous tensor of shape [B_c, M, D]")
+        K_u2, K_c, M2, D2 = self.dims
+        if (K_u, C.shape[1], M, D) != (K_u2, K_c, M2, D2) or tuple(W_c.shape) != (M2, K_c) \
+                or tuple(C.shape[2:]) != (D2,) or tuple(W_u.shape) != (M2, K_u2) or mp.shape != (B_c,):
+            raise IkboError(IKBO_ERR_INVALID_ARG, "shape differs from the plan")
+        st = self.forward_ptrs(U.data_ptr(), C.data_ptr(), mp.data_ptr(), W_u.data_ptr(), W_c.data_ptr(),
+                               out.data_ptr(), B_u, B_c, _stream_handle(stream))
+        if st != IKBO_OK:
+            raise IkboError(st, "ikbo_lce_forward")
+        return out
+
+    def check(self, stream=None) -> int:
+        """Synchronise and return (and clear) the device-side status."""
+        return lib().ikbo_lce_check(self.handle, _stream_handle(stream))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            st = lib().ikbo_lce_plan_destroy(self._h)
+            self._h = None
+            if st != IKBO_OK:
+                raise IkboError(st, "ikbo_lce_plan_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def lce_forward(U, C, mp, W_u, W_c, variant: str = "auto"):
+    """One-shot forward with a temporary plan sized to these inputs."""
+    torch = _torch()
+    dtype = "bf16" if U.dtype == torch.bfloat16 else "f32"
+    B_u, K_u, D = U.shape
+    B_c, K_c, _ = C.shape
+    M = W_u.shape[0]
+    with LcePlan(B_u, B_c, K_u, K_c, M, D, dtype=dtype, variant=variant) as plan:
+        Y = plan.forward(U, C, mp, W_u, W_c)
+        st = plan.check()
+        if st != IKBO_OK:
+            raise IkboError(st, "device status")
+        return Y

@@ -1,0 +1,108 @@
+// lce_internal.h -- host-side interface between the C ABI (ikbo_api.cpp) and the
+// kernels (lce_kernels.hip, lce_fused.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ikbo {
+
+enum DType { DT_BF16 = 0, DT_F32 = 1 };
+
+// Epilogue of the tile engine.
+enum Epi {
+    EPI_STORE_F32 = 0,  // out = acc (float32), e.g. the user partial P_u or the candidate partial P_c
+    EPI_ADD_USER = 1,   // out = T(acc + P_u[map[b]])  (gather-add epilogue)
+    EPI_STORE_T = 2     // out = T(acc)
+};
+
+// Device error bits (OR-ed into the plan's error word).
+enum : uint32_t { ERRBIT_MAP = 1u, ERRBIT_TIMEOUT = 2u };
+
+// One flat-column GEMM: for every batch entry b < B,
+//   out[b] (M x D) = W (M x K) . X[b] (K x D)   (+ epilogue)
+// The engine views the B*D output columns as one flat axis n = b*D + d and tiles
+// it in groups of 16*vec columns; each wave owns 16*mb rows of one group.
+struct TileGemmArgs {
+    const void *X;        // [B][K][D] elements of the plan's dtype
+    const void *W;        // packed: [M_pad][ldw], zero padded; unpacked: [M][K]
+    void *out;            // float [B][M][D] for EPI_STORE_F32, else dtype [B][M][D]
+    const float *P_u;     // EPI_ADD_USER: float [B_u][M][D]
+    const int32_t *map;   // EPI_ADD_USER: [B]
+    uint32_t *err;        // device error word
+    long long BD;         // B * D
+    int B, K, M, D, ldw, B_u;
+    int n_ks_full;        // number of 32-row K steps with no row past K
+    int n_ks;             // number of 32-row K steps (ceil(K / 32))
+    int n_mchunks;        // ceil(ceil(M/16) / mb)
+};
+
+struct TileConfig {
+    int vec;        // columns per lane slot: bf16 8 (16-byte loads) or 2 (4-byte); f32 4 or 1
+    int mb;         // 16-row MFMA blocks per wave
+    bool packed;    // A operand read from the zero-padded [M_pad][ldw] copy
+    int wpb;        // waves per block
+};
+
+hipError_t launch_tile_gemm(int dtype, int epi, const TileConfig &cfg, const TileGemmArgs &a,
+                            hipStream_t s);
+
+// Zero-padded copy of the projection for 16-byte A-operand loads:
+// out[m][k] for m < M_pad, k < ldw = W_a's K_a columns, then W_b's K_b columns
+// (W_b may be null), then zeros; rows m >= M are zero.
+struct PackJob {
+    const void *W_a;
+    const void *W_b;
+    void *out;
+    int K_a, K_b, ldw;
+};
+hipError_t launch_pack_w(int dtype, const PackJob *jobs, int n_jobs, int M, int M_pad, hipStream_t s);
+
+// X[b] = [U[map[b]] ; C[b]]  ([B_c][K_u + K_c][D]); map entries outside [0, B_u) set ERRBIT_MAP.
+hipError_t launch_gather_concat(int dtype, const void *U, const void *C, const int32_t *map, void *X,
+                                int B_u, int B_c, int K_u, int K_c, int D, uint32_t *err,
+                                hipStream_t s);
+
+// P_b[b] = P_u[map[b]]  (float [B_c][M][D]).
+hipError_t launch_bcast_rows(const float *P_u, const int32_t *map, float *P_b, int B_u, int B_c,
+                             int M, int D, uint32_t *err, hipStream_t s);
+
+// Y = dtype(P_c + P_b), elementwise over n elements.
+hipError_t launch_add_cast(int dtype, const float *P_c, const float *P_b, void *Y, long long n,
+                           hipStream_t s);
+
+// ---- single-launch fused forward (S4) -------------------------------------------------
+
+struct FusedArgs {
+    const void *U, *C, *W_u, *W_c;
+    const int32_t *map;
+    void *Y;
+    void *W_u_pad, *W_c_pad;     // [M_pad][ldw_u], [M_pad][ldw_c] packed in-kernel
+    float *P_u;                  // [B_u][M][D]
+    float *P_part;               // [ksplit-1][B_u][M][D] split-K partials of user tiles
+    uint32_t *ctr;               // [n_user_units] split-K arrival counters (monotonic)
+    uint32_t *flags;             // [2*n_mchunks] W-pack flags, then [n_user_units] user flags (epochs)
+    uint32_t *state;             // [0]=epoch, [1]=ticket, [2]=waves finished
+    uint32_t *err;
+    long long BD_u, BD_c;        // B_u*D, B_c*D
+    int B_u, B_c, K_u, K_c, M, D;
+    int ldw_u, ldw_c, M_pad;
+    int n_ks_u, n_ks_c, n_ks_full_u, n_ks_full_c;
+    int ksplit;                  // user K split factor
+    int ks_per_split;            // user K steps per split
+    int n_mchunks;
+    int n_ucols;                 // user column tiles
+    int n_user_units;            // n_ucols * n_mchunks (flags / counters)
+    int n_pack_units;            // 2 * n_mchunks (W_u and W_c, one unit per M chunk)
+    int n_units_total;           // wave units: pack + (user col tiles * ksplit + cand col tiles) * n_mchunks
+    int n_ccols;                 // candidate column tiles
+    uint32_t spin_limit;
+    uint32_t debug_flags;
+};
+
+hipError_t launch_fused(int dtype, const TileConfig &cfg, const FusedArgs &a, int grid,
+                        hipStream_t s);
+int fused_blocks_per_cu(int dtype, const TileConfig &cfg);
+
+}  // namespace ikbo

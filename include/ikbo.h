@@ -1,0 +1,149 @@
+/*
+ * ikbo.h -- C ABI of libikbo: the IKBO Linear Compression Embedding forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (IKBO recsys blog, "Deep Dive: Linear Compression"; aibriefing
+ * article, "kernel deep-dive case 1"):
+ *
+ *     Y[b] = W_u . U[map[b]]  +  W_c . C[b]          for b < B_c
+ *
+ * U holds the request-only (user) embeddings at their own batch B_u, C the
+ * per-candidate embeddings at batch B_c, and map[b] names the user of
+ * candidate b.  The kernels take the two batches "in their natural, mismatched
+ * sizes" plus the candidate-to-user map (blog, "Why broadcast is a data-layout
+ * problem" and "How the IKBO co-design is built"; aibriefing, RO/NRO paragraph)
+ * and never build the replicated tensor U[map].
+ *
+ * Layouts.  Every tensor is dense row-major (C order) in device memory owned by
+ * the caller:
+ *     U   [B_u, K_u, D]      C   [B_c, K_c, D]      map [B_c] int32
+ *     W_u [M, K_u]           W_c [M, K_c]           Y   [B_c, M, D]
+ * U, C, W_u, W_c and Y share one element type (bfloat16 or float32).  Products
+ * accumulate in float32; the user partial W_u.U[u] is kept in float32; Y is
+ * rounded once (round-to-nearest-even) when it is stored.
+ *
+ * Threading.  A plan may be used from one host thread and one stream at a
+ * time.  Different plans are independent.  No C++ exception crosses this ABI.
+ */
+#ifndef IKBO_H
+#define IKBO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque plan handle; created by ikbo_lce_plan, owned by the library. */
+typedef struct ikbo_lce_plan_s *ikbo_lce_plan_t;
+
+/* Status codes returned by every entry point. */
+enum {
+    IKBO_OK = 0,
+    IKBO_ERR_INVALID_ARG = -1,  /* null pointer, bad dimension, shape differs from the plan */
+    IKBO_ERR_UNSUPPORTED = -2,  /* valid but not implemented (e.g. D*elt not a multiple of 16 B) */
+    IKBO_ERR_HIP = -3,          /* a HIP runtime call failed; see ikbo_last_error_message() */
+    IKBO_ERR_ALIGNMENT = -4,    /* a tensor base address is not 16-byte aligned */
+    IKBO_ERR_TIMEOUT = -5,      /* device: a candidate tile gave up waiting for its user partial */
+    IKBO_ERR_MAP_RANGE = -6     /* device: some map[b] lies outside [0, B_u) */
+};
+
+/* Element type of U, C, W_u, W_c and Y. */
+enum { IKBO_DTYPE_BF16 = 0, IKBO_DTYPE_F32 = 1 };
+
+/*
+ * Kernel variant.  S0..S4 reproduce the pages' optimisation ladder on CDNA4
+ * (blog, "Deep Dive: Linear Compression", stages 1-4; zubnet summary, the
+ * four-stage paragraph); all five compute the same Y.
+ *   S0  materialise X = [U[map] ; C] in HBM, then one batched GEMM with [W_u | W_c];
+ *   S1  decompose by linearity (user GEMM at B_u rows, candidate GEMM at B_c rows),
+ *       then materialise P_u[map] and add; unpadded K, 4-byte operand loads;
+ *   S2  S1 with K zero-padded and 16-byte operand loads;
+ *   S3  user GEMM, then a candidate GEMM whose epilogue gathers P_u[map[b]] by
+ *       index and adds it in registers;
+ *   S4  one launch: user and candidate tiles overlap, candidate epilogues wait for
+ *       their user partial through device-scope release/acquire flags.
+ * AUTO selects S4.
+ */
+enum {
+    IKBO_VARIANT_AUTO = 0,
+    IKBO_S0_MATERIALISED = 1,
+    IKBO_S1_DECOMPOSED = 2,
+    IKBO_S2_ALIGNED = 3,
+    IKBO_S3_EPILOGUE_FUSED = 4,
+    IKBO_S4_PERSISTENT = 5
+};
+
+/* Plan flags (host-forced test conditions; production callers pass 0). */
+enum {
+    IKBO_FLAG_DEBUG_DELAY_USER = 2, /* S4: user tiles sleep before computing (exercises the wait) */
+    IKBO_FLAG_DEBUG_SKIP_USER = 4   /* S4: user tiles publish nothing; candidates time out */
+};
+
+/*
+ * Create a plan for one shape range ("the compiler needs each operator's
+ * dynamic shape range to pick the kernel": blog, co-design section; aibriefing,
+ * three-layers paragraph).  Chooses the tile configuration and allocates the
+ * device workspace (hipMalloc) on the current device; forward never allocates.
+ *   max_B_u, max_B_c  upper bounds of B_u and B_c in later forwards (>= 1, >= 0)
+ *   K_u, K_c, M, D    fixed dimensions (>= 1)
+ *   dtype             IKBO_DTYPE_*
+ *   variant           IKBO_VARIANT_AUTO or IKBO_S*
+ * On success stores a handle in *plan and returns IKBO_OK; on failure *plan is
+ * left NULL and nothing stays allocated.  Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+int ikbo_lce_plan(ikbo_lce_plan_t *plan, int max_B_u, int max_B_c, int K_u, int K_c,
+                  int M, int D, int dtype, int variant, unsigned flags);
+
+/*
+ * Enqueue Y[b] = W_u.U[map[b]] + W_c.C[b] on `stream` (a hipStream_t; NULL =
+ * the null stream).  All pointers are device pointers with the layouts above;
+ * U, C, W_u, W_c and Y must be 16-byte aligned.  The dimensions must equal the
+ * plan's, with 1 <= B_u <= max_B_u and 0 <= B_c <= max_B_c; B_c = 0 is a no-op.
+ * Host-side validation errors return before anything is enqueued.  The call is
+ * asynchronous: device-side conditions (map entry out of range, S4 wait
+ * timeout) are recorded in the plan and reported by ikbo_lce_check; the Y rows
+ * of an affected candidate are then unspecified.  Must be called with the
+ * plan's device current.
+ */
+int ikbo_lce_forward(ikbo_lce_plan_t plan, const void *U, const void *C, const int32_t *map,
+                     const void *W_u, const void *W_c, void *Y,
+                     int B_u, int B_c, int K_u, int K_c, int M, int D, void *stream);
+
+/*
+ * Wait for `stream`, then return and clear the device-side status recorded by
+ * earlier forwards on this plan (IKBO_OK, IKBO_ERR_MAP_RANGE or
+ * IKBO_ERR_TIMEOUT), or IKBO_ERR_HIP if the wait itself failed.
+ */
+int ikbo_lce_check(ikbo_lce_plan_t plan, void *stream);
+
+/*
+ * Write a NUL-terminated JSON description of the plan (variant, tile sizes,
+ * padded K, grid, workspace bytes) into json[0..cap).  Returns the length it
+ * needed (excluding the NUL), or a negative status.
+ */
+int ikbo_lce_plan_info(ikbo_lce_plan_t plan, char *json, size_t cap);
+
+/*
+ * Upper bound on the polling iterations a candidate tile spends waiting for a
+ * user partial (S4) before it records IKBO_ERR_TIMEOUT and moves on; 0 restores
+ * the default.  A test hook: every kernel exits even if a user tile never
+ * publishes.
+ */
+int ikbo_lce_plan_set_spin_limit(ikbo_lce_plan_t plan, uint32_t max_polls);
+
+/* Free the plan and its workspace (synchronises the device first).  NULL is a no-op. */
+int ikbo_lce_plan_destroy(ikbo_lce_plan_t plan);
+
+/* Static text for a status code. */
+const char *ikbo_status_str(int status);
+
+/* Text of the last IKBO_ERR_HIP failure seen by the calling host thread ("" if none). */
+const char *ikbo_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IKBO_H */

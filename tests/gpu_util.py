@@ -1,0 +1,65 @@
+"""Helpers for the GPU tests: device transfer of seeded inputs, readback, and a
+per-session cache of inputs and oracle outputs."""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+
+from broadcast_gemm_amd.inputs import CONFIG_BY_NAME, CONFIGS, bf16_bits_to_f32, make_inputs
+
+VARIANTS = ["S0", "S1", "S2", "S3", "S4"]
+ATOL, RTOL = 1e-3, 1.6e-2        # |Y_gpu - Y_ref| <= ATOL + RTOL*|Y_ref|  (bf16 in, fp32 accumulate)
+# Candidates the oracle evaluates one by one at the largest configuration.
+SAMPLED_ROWS = {"extreme-10000to1": [0, 1, 2, 4999, 9998, 9999, 10000, 10001, 15000, 19997, 19998, 19999]}
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray):
+    t = torch()
+    if a.dtype == np.uint16:
+        return t.from_numpy(a.view(np.int16)).view(t.bfloat16).to("cuda")
+    return t.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def to_f64(y) -> np.ndarray:
+    t = torch()
+    if y.dtype == t.bfloat16:
+        return bf16_bits_to_f32(y.view(t.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return y.detach().cpu().numpy().astype(np.float64)
+
+
+def dev_inputs(x):
+    return tuple(to_dev(a) for a in (x.U, x.C, x.map, x.W_u, x.W_c))
+
+
+@functools.lru_cache(maxsize=2)
+def cached_inputs(name: str):
+    return make_inputs(CONFIG_BY_NAME[name])
+
+
+@functools.lru_cache(maxsize=4)
+def cached_oracle(name: str):
+    import oracle
+    x = cached_inputs(name)
+    rows = SAMPLED_ROWS.get(name)
+    return oracle.lce_f64(x.U, x.C, x.map, x.W_u, x.W_c, rows=rows), rows
+
+
+def assert_close(Y_gpu: np.ndarray, Y_ref: np.ndarray, what: str):
+    import oracle
+    nbad, excess = oracle.tolerance_violations(Y_gpu, Y_ref, ATOL, RTOL)
+    assert nbad == 0, f"{what}: {nbad} of {Y_ref.size} elements outside tolerance (max excess {excess:.3g})"
+
+
+CONFIG_NAMES = [c.name for c in CONFIGS]
