@@ -2,10 +2,10 @@
 // the per-stage kernels and the single-launch fused kernel.
 //
 // Each wave accumulates acc[mb][t] for 16*MB rows (mrow0 ..) of W times one
-// group of 16*VEC flat columns.  Loads of step ks+1 are issued before the
-// MFMAs of step ks (register double buffering).  `pre()` runs once, after the
-// first step's loads are in flight and before the first A-operand load; the
-// fused kernel waits there for the packed weights.
+// group of 16*VEC flat columns.  Both operands of step ks+1 are loaded before
+// the MFMAs of step ks (register double buffering).  `pre()` runs once, after
+// the first step's B loads are in flight and before the first A-operand load;
+// the fused kernel waits there for the packed weights.
 #pragma once
 
 #include "lce_device.h"
@@ -47,6 +47,14 @@ __device__ __forceinline__ float load_a_f32(const float *__restrict__ W, int ldw
     }
 }
 
+// Compiler-only barrier: keeps the next step's loads issued before this step's
+// MFMAs.  Without it the prefetch is sunk below the MFMAs (shorter register live
+// ranges) and every K step waits a full memory round trip.
+__device__ __forceinline__ void pin_loads_above() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 struct NoPre {
     __device__ __forceinline__ void operator()() const {}
 };
@@ -67,41 +75,49 @@ __device__ __forceinline__ void mainloop_bf16(f32x4_t (&acc)[MB][VEC], const uin
         pre();
         return;
     }
-    RowBits<VEC> cur[8], nxt[8];
-    auto load_full = [&](RowBits<VEC>(&dst)[8], int ks) {
-        const uint16_t *p = xcol + (size_t)(ks * 32 + 8 * g) * D;
+    // Both operands of step ks+1 are requested before the MFMAs of step ks.  Vector
+    // memory counters retire in issue order and the compiler's wait counts take the
+    // most conservative path, so the loop body is branch-free: every iteration
+    // issues the same loads (the last prefetch re-reads an in-bounds step), rows
+    // past K are clamped at load and zeroed by a select at use, and the two register
+    // buffers alternate (copying a register with a load in flight forces a wait).
+    RowBits<VEC> rb0[8], rb1[8];
+    u32x4_t ab0[MB], ab1[MB];
+    auto load_b = [&](RowBits<VEC>(&dst)[8], int ks) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) dst[r] = load_row<VEC>(p + r * D);
+        for (int r = 0; r < 8; ++r)
+            dst[r] = load_row<VEC>(xcol + (size_t)imin_t(ks * 32 + 8 * g + r, K - 1) * D);
     };
-    // Rows at or past K read the last valid row (always in bounds) and are replaced
-    // by zeros, so a neighbouring matrix's data never enters the sum.
-    auto load_tail = [&](RowBits<VEC>(&dst)[8], int ks) {
+    auto load_a = [&](u32x4_t (&adst)[MB], int ks) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int k = ks * 32 + 8 * g + r;
-            RowBits<VEC> v = load_row<VEC>(xcol + (size_t)imin_t(k, K - 1) * D);
-            dst[r] = (k < K) ? v : zero_row<VEC>();
-        }
+        for (int mb = 0; mb < MB; ++mb)
+            adst[mb] = load_a_bf16<PACKED>(W, ldw, M, K, mrow0 + 16 * mb + j, ks * 32 + 8 * g);
     };
-    auto compute = [&](const RowBits<VEC>(&src)[8], int ks) {
+    auto compute = [&](RowBits<VEC>(&src)[8], const u32x4_t (&av)[MB], int ks) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) src[r] = (ks * 32 + 8 * g + r < K) ? src[r] : zero_row<VEC>();
         u32x4_t bop[VEC];
         transpose_rows<VEC>(src, bop);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const u32x4_t av = load_a_bf16<PACKED>(W, ldw, M, K, mrow0 + 16 * mb + j, ks * 32 + 8 * g);
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int t = 0; t < VEC; ++t) acc[mb][t] = mfma_bf16(av, bop[t], acc[mb][t]);
-        }
+            for (int t = 0; t < VEC; ++t) acc[mb][t] = mfma_bf16(av[mb], bop[t], acc[mb][t]);
     };
-    if (ks0 < nfull) load_full(cur, ks0); else load_tail(cur, ks0);
+    (void)nfull;
+    const int last = ks1 - 1;
+    load_b(rb0, ks0);          // B rows of the first step go out before pre(), its A after
     pre();
-    for (int ks = ks0; ks < ks1; ++ks) {
-        if (ks + 1 < ks1) {
-            if (ks + 1 < nfull) load_full(nxt, ks + 1); else load_tail(nxt, ks + 1);
-        }
-        compute(cur, ks);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) cur[r] = nxt[r];
+    load_a(ab0, ks0);
+    for (int ks = ks0; ks < ks1; ks += 2) {
+        load_b(rb1, imin_t(ks + 1, last));
+        load_a(ab1, imin_t(ks + 1, last));
+        pin_loads_above();
+        compute(rb0, ab0, ks);
+        if (ks + 1 >= ks1) break;
+        load_b(rb0, imin_t(ks + 2, last));
+        load_a(ab0, imin_t(ks + 2, last));
+        pin_loads_above();
+        compute(rb1, ab1, ks + 1);
     }
 }
 
@@ -120,39 +136,46 @@ __device__ __forceinline__ void mainloop_f32(f32x4_t (&acc)[MB][VEC], const floa
         pre();
         return;
     }
-    RowF32<VEC> cur[8], nxt[8];
-    auto load_full = [&](RowF32<VEC>(&dst)[8], int ks) {
+    RowF32<VEC> rb0[8], rb1[8];
+    float ab0[8][MB], ab1[8][MB];
+    auto load_a = [&](float (&dst)[8][MB], int ks) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) dst[s] = load_rowf<VEC>(xcol + (size_t)(ks * 32 + 4 * s + g) * D);
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                dst[s][mb] = load_a_f32<PACKED>(W, ldw, M, K, mrow0 + 16 * mb + j, ks * 32 + 4 * s + g);
     };
-    auto load_tail = [&](RowF32<VEC>(&dst)[8], int ks) {
+    auto load_b = [&](RowF32<VEC>(&dst)[8], int ks) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int k = ks * 32 + 4 * s + g;
-            RowF32<VEC> v = load_rowf<VEC>(xcol + (size_t)imin_t(k, K - 1) * D);
-            dst[s] = (k < K) ? v : zero_rowf<VEC>();
-        }
+        for (int s = 0; s < 8; ++s)
+            dst[s] = load_rowf<VEC>(xcol + (size_t)imin_t(ks * 32 + 4 * s + g, K - 1) * D);
     };
-    auto compute = [&](const RowF32<VEC>(&src)[8], int ks) {
+    auto compute = [&](RowF32<VEC>(&src)[8], const float (&av)[8][MB], int ks) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
+        for (int s = 0; s < 8; ++s) src[s] = (ks * 32 + 4 * s + g < K) ? src[s] : zero_rowf<VEC>();
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const float av = load_a_f32<PACKED>(W, ldw, M, K, mrow0 + 16 * mb + j, ks * 32 + 4 * s + g);
+        for (int s = 0; s < 8; ++s)
 #pragma unroll
-                for (int t = 0; t < VEC; ++t) acc[mb][t] = mfma_f32(av, rowf_elem<VEC>(src[s], t), acc[mb][t]);
-            }
-        }
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int t = 0; t < VEC; ++t)
+                    acc[mb][t] = mfma_f32(av[s][mb], rowf_elem<VEC>(src[s], t), acc[mb][t]);
     };
-    if (ks0 < nfull) load_full(cur, ks0); else load_tail(cur, ks0);
+    (void)nfull;
+    const int last = ks1 - 1;
+    load_b(rb0, ks0);
     pre();
-    for (int ks = ks0; ks < ks1; ++ks) {
-        if (ks + 1 < ks1) {
-            if (ks + 1 < nfull) load_full(nxt, ks + 1); else load_tail(nxt, ks + 1);
-        }
-        compute(cur, ks);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) cur[s] = nxt[s];
+    load_a(ab0, ks0);
+    for (int ks = ks0; ks < ks1; ks += 2) {
+        load_b(rb1, imin_t(ks + 1, last));
+        load_a(ab1, imin_t(ks + 1, last));
+        pin_loads_above();
+        compute(rb0, ab0, ks);
+        if (ks + 1 >= ks1) break;
+        load_b(rb0, imin_t(ks + 2, last));
+        load_a(ab0, imin_t(ks + 2, last));
+        pin_loads_above();
+        compute(rb1, ab1, ks + 1);
     }
 }
 
