@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libikbo.so")
-SOURCES = ["ikbo_api.cpp", "lce_kernels.hip", "lce_fused.hip"]
+SOURCES = ["ikbo_api.cpp", "lce_kernels.hip", "lce_fused.hip", "lce_rows.hip"]
 ARCH = os.environ.get("IKBO_OFFLOAD_ARCH", "gfx950")
 
 
@@ -32,16 +32,18 @@ def build(verbose: bool = False) -> str:
               "-I", CSRC, "-Wall", "-Wno-unused-function",
               # Packed fp32 VALU forms stay off in generated code.
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-    objs = []
+    jobs = []
     for src in SOURCES:
         obj = os.path.join(out_dir, src + ".o")
-        lang = ["-x", "hip"]
-        cmd = [hipcc()] + common + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc()] + common + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        msgs = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
-        if r.returncode != 0:
+        jobs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    objs = []
+    for src, obj, proc in jobs:
+        _, err = proc.communicate()
+        msgs = "\n".join(l for l in (err or "").splitlines() if "packed-fp32-ops" not in l)
+        if proc.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{msgs}")
         if verbose and msgs.strip():
             print(msgs)

@@ -1,38 +1,59 @@
 // ikbo_api.cpp -- the C ABI declared in include/ikbo.h: plans, validation,
 // workspace, and the launch sequence of each ladder stage.
+//
+// Two engines compute the products:
+//   rows  -- one wave per (batch entry, M chunk), all D columns of the entry,
+//            projection staged in LDS (lce_rows.hip); bf16 with D in
+//            {32, 64, 128, 160, 192} when the staged projection fits in LDS;
+//   flat  -- one wave per (128 flat columns, M chunk) over the B*D output
+//            columns (lce_kernels.hip, lce_fused.hip); every other case, and the
+//            narrow-load ladder stage S1.
 #include "ikbo.h"
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
 
 #include "lce_internal.h"
+#include "lce_rowtile.h"
 
 using namespace ikbo;
+
+namespace {
+
+enum Engine { ENGINE_FLAT = 0, ENGINE_ROWS = 1 };
+
+}  // namespace
 
 struct ikbo_lce_plan_s {
     int max_B_u, max_B_c, K_u, K_c, M, D, dtype, variant;
     unsigned flags;
-    int device;
+    int device, n_cu, max_lds;
     int elt;
+    int engine;
+    // flat engine
     TileConfig tile;
     int n_mblocks, n_mchunks, M_pad;
     int ldw_u, ldw_c, ldw_cat;      // padded K (multiples of 32)
-    // S4 (fused) schedule
-    int ksplit, ks_per_split, n_ucols_max, fused_grid, fused_bpc;
+    int n_ucols_max, fused_grid, fused_bpc;
+    // rows engine
+    int rows_mb;
+    int bpc_user, bpc_cand, bpc_both;
+    // user split-K (fused paths and the rows engine's user launches)
+    int ksplit, ks_per_split;
     uint32_t spin_limit;
+    uint32_t epoch;                 // last epoch handed to a same-launch user/candidate forward
     // workspace (one hipMalloc arena)
     char *arena;
     size_t arena_bytes;
     void *W_u_pad, *W_c_pad, *W_cat_pad, *X;
     float *P_u, *P_c, *P_b, *P_part;
     uint32_t *err, *ctr, *flagw, *state;
-    size_t n_flag_words;
 };
 
 namespace {
@@ -49,11 +70,10 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 const uint32_t kDefaultSpin = 1u << 20;   // polls of about 1 us each
 
-// Choose the number of 16-row blocks per wave: fewest wasted blocks, then the
-// largest chunk (fewer waves re-reading the same activation columns).
-int choose_mb(int n_mblocks) {
+// Blocks of 16 rows per wave: fewest wasted blocks, then the largest chunk.
+int choose_mb(int n_mblocks, int max_mb) {
     int best = 1, best_waste = 1 << 30;
-    for (int mb = 4; mb >= 1; --mb) {
+    for (int mb = max_mb; mb >= 1; --mb) {
         int waste = ceil_div(n_mblocks, mb) * mb - n_mblocks;
         if (waste < best_waste) { best = mb; best_waste = waste; }
     }
@@ -61,6 +81,12 @@ int choose_mb(int n_mblocks) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int env_int(const char *name, int dflt) {
+    const char *v = getenv(name);
+    if (v == nullptr || *v == '\0') return dflt;
+    return atoi(v);
+}
 
 }  // namespace
 
@@ -93,8 +119,9 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     const int elt = dtype == IKBO_DTYPE_BF16 ? 2 : 4;
     // Rows of D elements must be whole 16-byte chunks (128-bit loads and stores).
     if ((long long)D * elt % 16 != 0) return IKBO_ERR_UNSUPPORTED;
-    // Flat column indices and per-matrix offsets stay within the kernels' integer ranges.
-    if ((long long)max_B_c * D >= (1LL << 40) || (long long)K_u + K_c > (1 << 24) || M > (1 << 20))
+    // Flat column indices and per-matrix byte offsets stay within the kernels' integer ranges.
+    if ((long long)max_B_c * D >= (1LL << 40) || (long long)K_u + K_c > (1 << 24) || M > (1 << 20) ||
+        (long long)(K_u + K_c) * D * elt >= (1LL << 31))
         return IKBO_ERR_UNSUPPORTED;
 
     ikbo_lce_plan_s *p = new (std::nothrow) ikbo_lce_plan_s();
@@ -104,32 +131,79 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     p->spin_limit = kDefaultSpin;
     hipError_t e = hipGetDevice(&p->device);
     if (e != hipSuccess) { delete p; return hip_fail(e, "hipGetDevice"); }
+    e = hipDeviceGetAttribute(&p->n_cu, hipDeviceAttributeMultiprocessorCount, p->device);
+    if (e != hipSuccess) { delete p; return hip_fail(e, "hipDeviceGetAttribute(CUs)"); }
+    int max_lds = 0;
+    e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, p->device);
+    p->max_lds = max_lds;
+    if (e != hipSuccess) { delete p; return hip_fail(e, "hipDeviceGetAttribute(LDS)"); }
 
-    const bool narrow = variant == IKBO_S1_DECOMPOSED;
-    p->tile.vec = dtype == IKBO_DTYPE_BF16 ? (narrow ? 2 : 8) : (narrow ? 1 : 4);
-    p->tile.packed = !narrow;
-    p->n_mblocks = ceil_div(M, 16);
-    p->tile.mb = choose_mb(p->n_mblocks);
-    p->n_mchunks = ceil_div(p->n_mblocks, p->tile.mb);
-    p->tile.wpb = std::min(p->n_mchunks, 4);
-    p->M_pad = p->n_mchunks * p->tile.mb * 16;
+    const int n_mblocks = ceil_div(M, 16);
+    p->n_mblocks = n_mblocks;
     p->ldw_u = ceil_div(K_u, 32) * 32;
     p->ldw_c = ceil_div(K_c, 32) * 32;
     p->ldw_cat = ceil_div(K_u + K_c, 32) * 32;
 
-    // Workspace layout by variant.
+    // ---- engine choice ----
+    p->engine = ENGINE_FLAT;
+    if (dtype == IKBO_DTYPE_BF16 && variant != IKBO_S1_DECOMPOSED && rows_supported(D)) {
+        const int mb = choose_mb(n_mblocks, rows_max_mb(D));
+        const int mpad = ceil_div(n_mblocks, mb) * mb * 16;
+        // The staged projections (as is, plus slack) must fit one workgroup's LDS.
+        const size_t lds_u = (size_t)lds_w_elems(M, K_u) * 2, lds_c = (size_t)lds_w_elems(M, K_c) * 2;
+        const size_t lds_cat = (size_t)lds_w_elems(M, ceil_div(K_u + K_c, 32) * 32) * 2;
+        bool fits;
+        if (variant == IKBO_S0_MATERIALISED) fits = lds_cat <= (size_t)max_lds;
+        else if (variant == IKBO_S4_PERSISTENT) fits = lds_u + lds_c <= (size_t)max_lds;
+        else fits = std::max(lds_u, lds_c) <= (size_t)max_lds;
+        // Epilogue byte offsets within one fp32 [M_pad][D] matrix are 32-bit.
+        if (fits && (long long)mpad * D * 4 < (1LL << 31)) {
+            p->engine = ENGINE_ROWS;
+            p->rows_mb = mb;
+            p->n_mchunks = ceil_div(n_mblocks, mb);
+            p->M_pad = mpad;
+        }
+    }
+    if (p->engine == ENGINE_FLAT) {
+        const bool narrow = variant == IKBO_S1_DECOMPOSED;
+        p->tile.vec = dtype == IKBO_DTYPE_BF16 ? (narrow ? 2 : 8) : (narrow ? 1 : 4);
+        p->tile.packed = !narrow;
+        p->tile.mb = choose_mb(n_mblocks, 4);
+        p->n_mchunks = ceil_div(n_mblocks, p->tile.mb);
+        p->tile.wpb = std::min(p->n_mchunks, 4);
+        p->M_pad = p->n_mchunks * p->tile.mb * 16;
+    }
+
+    // ---- user K split (flat engine's fused kernel; the rows engine streams all of K) ----
+    const int n_ks_u = ceil_div(K_u, 32), n_ks_c = ceil_div(K_c, 32);
+    int kps;
+    if (p->engine == ENGINE_ROWS)
+        kps = n_ks_u;
+    else
+        kps = env_int("IKBO_USER_KSTEPS", std::max(1, n_ks_c - 2));
+    kps = std::max(1, std::min(kps, n_ks_u));
+    p->ksplit = ceil_div(n_ks_u, kps);
+    p->ks_per_split = ceil_div(n_ks_u, p->ksplit);
+    p->ksplit = ceil_div(n_ks_u, p->ks_per_split);
+    p->n_ucols_max = (int)(((long long)max_B_u * D + 127) / 128);
+
+    // ---- workspace ----
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes, 256); return at; };
     const size_t o_err = take(64);
-    size_t o_wu = 0, o_wc = 0, o_wcat = 0, o_x = 0, o_pu = 0, o_pc = 0, o_pb = 0, o_part = 0;
-    size_t o_ctr = 0, o_flag = 0, o_state = 0;
+    const size_t o_state = take(64);
     const size_t pu_bytes = (size_t)max_B_u * M * D * 4;
     const size_t pc_bytes = (size_t)max_B_c * M * D * 4;
+    const size_t n_units = (size_t)std::max(p->n_ucols_max, max_B_u) * p->n_mchunks;
+    const size_t o_ctr = take(n_units * 4);
+    const size_t o_flag = take((n_units + 2 + 2 * (size_t)p->n_mchunks) * 4);
+    size_t o_wu = 0, o_wc = 0, o_wcat = 0, o_x = 0, o_pu = 0, o_pc = 0, o_pb = 0, o_part = 0;
+    const bool flat = p->engine == ENGINE_FLAT;
     if (variant == IKBO_S0_MATERIALISED) {
         o_wcat = take((size_t)p->M_pad * p->ldw_cat * elt);
         o_x = take((size_t)max_B_c * (K_u + K_c) * D * elt);
     } else {
-        if (variant != IKBO_S1_DECOMPOSED) {
+        if (flat && variant != IKBO_S1_DECOMPOSED) {
             o_wu = take((size_t)p->M_pad * p->ldw_u * elt);
             o_wc = take((size_t)p->M_pad * p->ldw_c * elt);
         }
@@ -138,22 +212,9 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
             o_pc = take(pc_bytes);
             o_pb = take(pc_bytes);
         }
-    }
-    if (variant == IKBO_S4_PERSISTENT) {
-        const int n_ks_u = ceil_div(K_u, 32), n_ks_c = ceil_div(K_c, 32);
-        // Split the user K loop so a user tile finishes well before a candidate tile
-        // reaches its epilogue.
-        int target = std::max(1, n_ks_c - 2);
-        p->ksplit = std::max(1, std::min(8, ceil_div(n_ks_u, target)));
-        p->ks_per_split = ceil_div(n_ks_u, p->ksplit);
-        p->ksplit = ceil_div(n_ks_u, p->ks_per_split);
-        p->n_ucols_max = (int)(((long long)max_B_u * D + 16 * p->tile.vec - 1) / (16 * p->tile.vec));
-        const size_t n_units = (size_t)p->n_ucols_max * p->n_mchunks;
-        if (p->ksplit > 1) o_part = take((size_t)(p->ksplit - 1) * pu_bytes);
-        o_ctr = take(n_units * 4);
-        p->n_flag_words = n_units + 2 * (size_t)p->n_mchunks;   // pack flags, then user flags
-        o_flag = take(p->n_flag_words * 4);
-        o_state = take(64);
+        // Partial user slices of the flat fused kernel (slice 0 is P_u itself).
+        if (flat && variant == IKBO_S4_PERSISTENT && p->ksplit > 1)
+            o_part = take((size_t)(p->ksplit - 1) * pu_bytes);
     }
     p->arena_bytes = off;
     e = hipMalloc(reinterpret_cast<void **>(&p->arena), p->arena_bytes);
@@ -162,6 +223,9 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     if (e != hipSuccess) { (void)hipFree(p->arena); delete p; return hip_fail(e, "hipMemset(workspace)"); }
     char *A = p->arena;
     p->err = reinterpret_cast<uint32_t *>(A + o_err);
+    p->state = reinterpret_cast<uint32_t *>(A + o_state);
+    p->ctr = reinterpret_cast<uint32_t *>(A + o_ctr);
+    p->flagw = reinterpret_cast<uint32_t *>(A + o_flag);
     p->W_u_pad = o_wu ? A + o_wu : nullptr;
     p->W_c_pad = o_wc ? A + o_wc : nullptr;
     p->W_cat_pad = o_wcat ? A + o_wcat : nullptr;
@@ -170,20 +234,36 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     p->P_c = o_pc ? reinterpret_cast<float *>(A + o_pc) : nullptr;
     p->P_b = o_pb ? reinterpret_cast<float *>(A + o_pb) : nullptr;
     p->P_part = o_part ? reinterpret_cast<float *>(A + o_part) : nullptr;
-    p->ctr = o_ctr ? reinterpret_cast<uint32_t *>(A + o_ctr) : nullptr;
-    p->flagw = o_flag ? reinterpret_cast<uint32_t *>(A + o_flag) : nullptr;
-    p->state = o_state ? reinterpret_cast<uint32_t *>(A + o_state) : nullptr;
-    if (variant == IKBO_S4_PERSISTENT) {
-        // Epoch starts at 1 so that the zeroed flags read as "not yet published".
-        const uint32_t one = 1;
-        e = hipMemcpy(p->state, &one, sizeof one, hipMemcpyHostToDevice);
-        if (e != hipSuccess) { (void)hipFree(p->arena); delete p; return hip_fail(e, "hipMemcpy(state)"); }
-        int n_cu = 0;
-        e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, p->device);
-        if (e != hipSuccess) { (void)hipFree(p->arena); delete p; return hip_fail(e, "hipDeviceGetAttribute"); }
+    // Epoch starts at 1 so that the zeroed flags read as "not yet published".
+    const uint32_t one = 1;
+    e = hipMemcpy(p->state, &one, sizeof one, hipMemcpyHostToDevice);
+    if (e != hipSuccess) { (void)hipFree(p->arena); delete p; return hip_fail(e, "hipMemcpy(state)"); }
+
+    // ---- persistent grid sizes ----
+    if (p->engine == ENGINE_ROWS) {
+        RowArgs r{};
+        r.M = M; r.M_pad = p->M_pad; r.K_u = K_u;
+        r.K_wc = variant == IKBO_S0_MATERIALISED ? p->ldw_cat : K_c;
+        const int epi = variant == IKBO_S0_MATERIALISED ? EPI_STORE_T
+                        : variant == IKBO_S2_ALIGNED     ? EPI_STORE_F32
+                                                         : EPI_ADD_USER;
+        auto bpc = [&](int nu, int nc) {
+            r.n_user = nu; r.n_cand = nc;
+            if (rows_lds_bytes(r) > (size_t)max_lds) return 0;
+            return rows_blocks_per_cu(epi, D, p->rows_mb, rows_lds_bytes(r));
+        };
+        p->bpc_user = variant == IKBO_S0_MATERIALISED ? 1 : bpc(1, 0);
+        p->bpc_cand = bpc(0, 1);
+        p->bpc_both = variant == IKBO_S4_PERSISTENT ? bpc(1, 1) : 1;
+        if (p->bpc_user < 1 || p->bpc_cand < 1 || p->bpc_both < 1) {
+            (void)hipFree(p->arena);
+            delete p;
+            return IKBO_ERR_UNSUPPORTED;
+        }
+    } else if (variant == IKBO_S4_PERSISTENT) {
         p->fused_bpc = fused_blocks_per_cu(dtype, p->tile);
         if (p->fused_bpc < 1) { (void)hipFree(p->arena); delete p; return IKBO_ERR_UNSUPPORTED; }
-        p->fused_grid = n_cu * p->fused_bpc;
+        p->fused_grid = p->n_cu * p->fused_bpc;
     }
     *out = p;
     return IKBO_OK;
@@ -212,17 +292,19 @@ int ikbo_lce_plan_destroy(ikbo_lce_plan_t p) {
 int ikbo_lce_plan_info(ikbo_lce_plan_t p, char *json, size_t cap) {
     if (p == nullptr || (json == nullptr && cap > 0)) return IKBO_ERR_INVALID_ARG;
     static const char *names[] = {"AUTO", "S0", "S1", "S2", "S3", "S4"};
+    const bool rows = p->engine == ENGINE_ROWS;
     char buf[1024];
     int n = snprintf(buf, sizeof buf,
-                     "{\"variant\":\"%s\",\"dtype\":\"%s\",\"max_B_u\":%d,\"max_B_c\":%d,\"K_u\":%d,"
-                     "\"K_c\":%d,\"M\":%d,\"D\":%d,\"vec\":%d,\"mb\":%d,\"waves_per_block\":%d,"
-                     "\"n_mchunks\":%d,\"M_pad\":%d,\"K_u_pad\":%d,\"K_c_pad\":%d,\"K_cat_pad\":%d,"
-                     "\"tile_cols\":%d,\"user_ksplit\":%d,\"fused_grid\":%d,\"fused_blocks_per_cu\":%d,"
-                     "\"workspace_bytes\":%zu}",
-                     names[p->variant], p->dtype == IKBO_DTYPE_BF16 ? "bf16" : "f32", p->max_B_u,
-                     p->max_B_c, p->K_u, p->K_c, p->M, p->D, p->tile.vec, p->tile.mb, p->tile.wpb,
-                     p->n_mchunks, p->M_pad, p->ldw_u, p->ldw_c, p->ldw_cat, 16 * p->tile.vec, p->ksplit,
-                     p->fused_grid, p->fused_bpc, p->arena_bytes);
+                     "{\"variant\":\"%s\",\"dtype\":\"%s\",\"engine\":\"%s\",\"max_B_u\":%d,\"max_B_c\":%d,"
+                     "\"K_u\":%d,\"K_c\":%d,\"M\":%d,\"D\":%d,\"mb\":%d,\"n_mchunks\":%d,\"M_pad\":%d,"
+                     "\"vec\":%d,\"K_u_pad\":%d,\"K_c_pad\":%d,\"K_cat_pad\":%d,\"user_ksplit\":%d,"
+                     "\"user_ksteps_per_split\":%d,\"blocks_per_cu\":[%d,%d,%d],\"fused_grid\":%d,"
+                     "\"n_cu\":%d,\"workspace_bytes\":%zu}",
+                     names[p->variant], p->dtype == IKBO_DTYPE_BF16 ? "bf16" : "f32", rows ? "rows" : "flat",
+                     p->max_B_u, p->max_B_c, p->K_u, p->K_c, p->M, p->D, rows ? p->rows_mb : p->tile.mb,
+                     p->n_mchunks, p->M_pad, rows ? 0 : p->tile.vec, p->ldw_u, p->ldw_c, p->ldw_cat, p->ksplit,
+                     p->ks_per_split, p->bpc_user, p->bpc_cand, p->bpc_both, p->fused_grid, p->n_cu,
+                     p->arena_bytes);
     if (n < 0) return IKBO_ERR_INVALID_ARG;
     if (cap > 0) {
         size_t c = std::min((size_t)n, cap - 1);
@@ -249,24 +331,110 @@ int ikbo_lce_check(ikbo_lce_plan_t p, void *stream) {
     return IKBO_OK;
 }
 
-int ikbo_lce_forward(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t *map,
-                     const void *W_u, const void *W_c, void *Y, int B_u, int B_c, int K_u, int K_c,
-                     int M, int D, void *stream) {
-    if (p == nullptr) return IKBO_ERR_INVALID_ARG;
-    if (K_u != p->K_u || K_c != p->K_c || M != p->M || D != p->D) return IKBO_ERR_INVALID_ARG;
-    if (B_c < 0 || B_c > p->max_B_c || B_u < 1 || B_u > p->max_B_u) return IKBO_ERR_INVALID_ARG;
-    if (B_c == 0) return IKBO_OK;
-    if (!U || !C || !map || !W_u || !W_c || !Y) return IKBO_ERR_INVALID_ARG;
-    if (!aligned16(U) || !aligned16(C) || !aligned16(Y) || !aligned16(W_u) || !aligned16(W_c) ||
-        (reinterpret_cast<uintptr_t>(map) & 3u) != 0)
-        return IKBO_ERR_ALIGNMENT;
-    int cur = -1;
-    hipError_t e = hipGetDevice(&cur);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    if (cur != p->device) return IKBO_ERR_INVALID_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int dt = p->dtype;
+namespace {
 
+// One launch of the rows engine with a.n_user user units and a.n_cand candidate units.
+hipError_t rows_launch(ikbo_lce_plan_t p, int epi, const RowArgs &a, int bpc, hipStream_t s) {
+    const int waves = a.n_user + a.n_cand;
+    if (waves == 0) return hipSuccess;
+    const int grid = std::max(1, std::min(p->n_cu * bpc, ceil_div(waves, kRowsBlock / 64)));
+    if (rows_lds_bytes(a) > (size_t)p->max_lds) return hipErrorInvalidValue;
+    return launch_rows(epi, p->rows_mb, a, grid, s);
+}
+
+int forward_rows(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t *map, const void *W_u,
+                 const void *W_c, void *Y, int B_u, int B_c, hipStream_t s) {
+    const int K_u = p->K_u, K_c = p->K_c, M = p->M, D = p->D, dt = p->dtype;
+    RowArgs a{};
+    a.U = static_cast<const uint16_t *>(U);
+    a.C = static_cast<const uint16_t *>(C);
+    a.W_u = static_cast<const uint16_t *>(W_u);
+    a.W_c = static_cast<const uint16_t *>(W_c);
+    a.map = map;
+    a.P_u = p->P_u;
+    a.flags = p->flagw;
+    a.err = p->err;
+    a.B_u = B_u; a.M = M; a.D = D; a.M_pad = p->M_pad;
+    a.K_u = K_u; a.K_c = K_c; a.K_wc = K_c;
+    a.n_ks_u = ceil_div(K_u, 32); a.n_ks_c = ceil_div(K_c, 32);
+    a.n_mchunks = p->n_mchunks;
+    a.spin_limit = p->spin_limit;
+    a.debug_flags = p->flags;
+    const int n_user = B_u * p->n_mchunks;
+    const int n_cand = B_c * p->n_mchunks;
+    hipError_t e;
+    switch (p->variant) {
+        case IKBO_S0_MATERIALISED: {
+            if ((e = launch_gather_concat(dt, U, C, map, p->X, B_u, B_c, K_u, K_c, D, p->err, s)) != hipSuccess)
+                return hip_fail(e, "gather_concat");
+            // [W_u | W_c], zero-padded to ldw_cat columns, is the materialised projection.
+            PackJob pj{W_u, W_c, p->W_cat_pad, K_u, K_c, p->ldw_cat};
+            if ((e = launch_pack_w(dt, &pj, 1, M, M, s)) != hipSuccess) return hip_fail(e, "pack_w");
+            RowArgs c = a;
+            c.C = static_cast<const uint16_t *>(p->X);
+            c.W_c = static_cast<const uint16_t *>(p->W_cat_pad); c.K_wc = p->ldw_cat;
+            c.K_c = K_u + K_c; c.n_ks_c = ceil_div(K_u + K_c, 32);
+            c.n_user = 0; c.n_cand = n_cand; c.out = Y;
+            if ((e = rows_launch(p, EPI_STORE_T, c, p->bpc_cand, s)) != hipSuccess) return hip_fail(e, "rows gemm");
+            break;
+        }
+        case IKBO_S2_ALIGNED: {
+            RowArgs u = a;
+            u.n_user = n_user; u.n_cand = 0;
+            if ((e = rows_launch(p, EPI_STORE_F32, u, p->bpc_user, s)) != hipSuccess) return hip_fail(e, "user gemm");
+            RowArgs c = a;
+            c.n_user = 0; c.n_cand = n_cand; c.out = p->P_c;
+            if ((e = rows_launch(p, EPI_STORE_F32, c, p->bpc_cand, s)) != hipSuccess) return hip_fail(e, "cand gemm");
+            if ((e = launch_bcast_rows(p->P_u, map, p->P_b, B_u, B_c, M, D, p->err, s)) != hipSuccess)
+                return hip_fail(e, "bcast");
+            if ((e = launch_add_cast(dt, p->P_c, p->P_b, Y, (long long)B_c * M * D, s)) != hipSuccess)
+                return hip_fail(e, "add_cast");
+            break;
+        }
+        case IKBO_S3_EPILOGUE_FUSED: {
+            RowArgs u = a;
+            u.n_user = n_user; u.n_cand = 0;
+            if ((e = rows_launch(p, EPI_ADD_USER, u, p->bpc_user, s)) != hipSuccess) return hip_fail(e, "user gemm");
+            RowArgs c = a;
+            c.n_user = 0; c.n_cand = n_cand; c.out = Y; c.wait_flags = 0;   // stream order publishes P_u
+            if ((e = rows_launch(p, EPI_ADD_USER, c, p->bpc_cand, s)) != hipSuccess) return hip_fail(e, "cand gemm");
+            break;
+        }
+        case IKBO_S4_PERSISTENT: {
+            // One launch needs a fresh epoch per forward.  A captured launch would replay a
+            // baked epoch and meet its own old flags, and a grid with fewer waves than user
+            // units could queue a user unit behind a waiting candidate: both take the
+            // two-launch sequence instead.
+            hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+            if ((e = hipStreamIsCapturing(s, &cap)) != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+            const int waves = std::max(1, std::min(p->n_cu * p->bpc_both, ceil_div(n_user + n_cand, kRowsBlock / 64))) *
+                              (kRowsBlock / 64);
+            if (cap == hipStreamCaptureStatusNone && n_user <= waves) {
+                RowArgs f = a;
+                f.n_user = n_user; f.n_cand = n_cand; f.out = Y; f.wait_flags = 1;
+                f.epoch = ++p->epoch;
+                if (f.epoch == 0) f.epoch = ++p->epoch;   // 0 is the flags' initial value
+                if ((e = rows_launch(p, EPI_ADD_USER, f, p->bpc_both, s)) != hipSuccess) return hip_fail(e, "fused");
+                break;
+            }
+            RowArgs u = a;
+            u.n_user = n_user; u.n_cand = 0;
+            if ((e = rows_launch(p, EPI_ADD_USER, u, p->bpc_user, s)) != hipSuccess) return hip_fail(e, "user gemm");
+            RowArgs c = a;
+            c.n_user = 0; c.n_cand = n_cand; c.out = Y; c.wait_flags = 0;
+            if ((e = rows_launch(p, EPI_ADD_USER, c, p->bpc_cand, s)) != hipSuccess) return hip_fail(e, "cand gemm");
+            break;
+        }
+        default:
+            return IKBO_ERR_INVALID_ARG;
+    }
+    return IKBO_OK;
+}
+
+int forward_flat(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t *map, const void *W_u,
+                 const void *W_c, void *Y, int B_u, int B_c, hipStream_t s) {
+    const int K_u = p->K_u, K_c = p->K_c, M = p->M, D = p->D, dt = p->dtype;
+    hipError_t e;
     auto gemm_args = [&](const void *X, const void *W, int ldw, int B, int K) {
         TileGemmArgs a{};
         a.X = X; a.W = W; a.ldw = ldw; a.B = B; a.K = K; a.M = M; a.D = D; a.B_u = B_u;
@@ -278,7 +446,6 @@ int ikbo_lce_forward(ikbo_lce_plan_t p, const void *U, const void *C, const int3
         a.map = map;
         return a;
     };
-
     switch (p->variant) {
         case IKBO_S0_MATERIALISED: {
             PackJob j{W_u, W_c, p->W_cat_pad, K_u, K_c, p->ldw_cat};
@@ -353,6 +520,28 @@ int ikbo_lce_forward(ikbo_lce_plan_t p, const void *U, const void *C, const int3
             return IKBO_ERR_INVALID_ARG;
     }
     return IKBO_OK;
+}
+
+}  // namespace
+
+int ikbo_lce_forward(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t *map,
+                     const void *W_u, const void *W_c, void *Y, int B_u, int B_c, int K_u, int K_c,
+                     int M, int D, void *stream) {
+    if (p == nullptr) return IKBO_ERR_INVALID_ARG;
+    if (K_u != p->K_u || K_c != p->K_c || M != p->M || D != p->D) return IKBO_ERR_INVALID_ARG;
+    if (B_c < 0 || B_c > p->max_B_c || B_u < 1 || B_u > p->max_B_u) return IKBO_ERR_INVALID_ARG;
+    if (B_c == 0) return IKBO_OK;
+    if (!U || !C || !map || !W_u || !W_c || !Y) return IKBO_ERR_INVALID_ARG;
+    if (!aligned16(U) || !aligned16(C) || !aligned16(Y) || !aligned16(W_u) || !aligned16(W_c) ||
+        (reinterpret_cast<uintptr_t>(map) & 3u) != 0)
+        return IKBO_ERR_ALIGNMENT;
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != p->device) return IKBO_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p->engine == ENGINE_ROWS) return forward_rows(p, U, C, map, W_u, W_c, Y, B_u, B_c, s);
+    return forward_flat(p, U, C, map, W_u, W_c, Y, B_u, B_c, s);
 }
 
 }  // extern "C"

@@ -20,6 +20,8 @@
 
 namespace ikbo {
 
+__device__ __forceinline__ int imin_t(int a, int b) { return a < b ? a : b; }
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));

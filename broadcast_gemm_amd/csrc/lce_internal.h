@@ -105,4 +105,36 @@ hipError_t launch_fused(int dtype, const TileConfig &cfg, const FusedArgs &a, in
                         hipStream_t s);
 int fused_blocks_per_cu(int dtype, const TileConfig &cfg);
 
+// ---- row-tile engine (bf16; D in {32, 64, 128, 160, 192}) ------------------------------
+
+constexpr int kRowsBlock = 256;   // 4 waves: one per SIMD, up to 512 registers each
+
+// Work of one launch: n_user user units, then n_cand candidate units (see lce_rows.hip).
+struct RowArgs {
+    const uint16_t *U, *C;        // U [B_u][K_u][D]; C [B][K_c][D] (the materialised X for S0)
+    const uint16_t *W_u;          // [M][K_u]
+    const uint16_t *W_c;          // candidate projection [M][K_wc] (rows K_wc long)
+    const int32_t *map;
+    void *out;                    // Y (bf16) or P_c (fp32)
+    float *P_u;                   // [B_u][M][D]
+    uint32_t *flags;              // [2 + B_u * n_mchunks] user flags (epochs) from index 2
+    uint32_t *err;
+    uint32_t epoch;               // value user units publish and candidates wait for
+    int B_u, M, D, M_pad;
+    int K_u, K_c, K_wc;           // K_c: rows of C[b]; K_wc >= K_c: row length of W_c (zero past K_c)
+    int n_ks_u, n_ks_c;
+    int n_mchunks;
+    int n_user, n_cand;           // work units in this launch
+    int wait_flags;               // users publish and candidates wait (users in the same launch)
+    uint32_t spin_limit;
+    uint32_t debug_flags;
+};
+
+bool rows_supported(int D);
+int rows_max_mb(int D);
+size_t rows_tile_bytes(const RowArgs &a);
+size_t rows_lds_bytes(const RowArgs &a);
+int rows_blocks_per_cu(int epi, int D, int mb, size_t lds_bytes);
+hipError_t launch_rows(int epi, int mb, const RowArgs &a, int grid, hipStream_t s);
+
 }  // namespace ikbo

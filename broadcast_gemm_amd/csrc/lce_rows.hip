@@ -1,0 +1,421 @@
+// lce_rows.hip -- persistent row-tile kernels for the IKBO LCE forward on gfx950.
+//
+// One kernel template serves the ladder stages that decompose the product (and
+// the materialised baseline).  A workgroup of four waves (one per SIMD, so each
+// wave may hold 512 registers) stages the projections it needs in LDS once, then
+// every wave works through a static list of units, wave w taking units w, w + T,
+// w + 2T, ... (T = waves in the grid).  Units are numbered
+//
+//   user units      [0, n_user): (u, mc) = rows [mc*16*MB, +16*MB) of
+//                   P_u[u] = W_u . U[u] in fp32 (IKBO recsys blog, "Deep Dive:
+//                   Linear Compression", stage 1: the user product at its own
+//                   batch size);
+//   candidate units [n_user, n_user + n_cand): (b, mc) = rows of W_c . C[b]; the
+//                   epilogue stores fp32 (unfused ladder stages), stores bf16
+//                   (baseline), or gathers P_u[map[b]] by index, adds it in
+//                   registers and stores Y once (stage 3), first waiting for flag
+//                   (map[b], mc) when the user units run in the same launch
+//                   (stage 4: one launch, user and candidate work overlapped).
+//
+// A wave streams the K steps of consecutive units through one register ring, so
+// the opening steps of its next unit are in flight during the current unit's
+// epilogue and the Y stores overlap the next reads.
+//
+// Publication without cache maintenance: a user unit writes P_u through to
+// memory (device-scope stores), waits for the acknowledgements and only then
+// stores the launch epoch in its flag.  A candidate that has read the flag
+// reads P_u with ordinary loads: no wave of the launch touched those lines
+// before they were final, and caches start the launch clean, so no cache can
+// hold an older copy.  Agent-scope fences would instead write back or
+// invalidate a whole L2 per use.
+//
+// There is no device-wide work counter: a single hot atomic serialises every
+// wave of the grid.  The host sizes the grid to be co-resident and guarantees
+// n_user <= T, so every user unit is the first unit of its wave and never sits
+// behind a wait; every poll is also bounded (a timeout is recorded and the wave
+// moves on).  The epoch is supplied per launch by the host.
+#include <algorithm>
+
+#include "lce_internal.h"
+#include "lce_rowtile.h"
+
+namespace ikbo {
+
+namespace {
+
+__device__ __forceinline__ uint32_t ld_flag(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_flag(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+constexpr int kSc1 = 16;   // buffer cache-policy bit sc1: device scope (write through this XCD's L2)
+
+// Wait until every store this wave issued has been acknowledged.  Stores made
+// with kSc1 are then visible to every XCD, and a flag or counter update issued
+// afterwards publishes them.  The asm also keeps the compiler from moving
+// memory operations across the wait.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Epilogue memory traffic goes through buffer resources that cover exactly one
+// [M][D] matrix: rows at or past M read as zero and their stores are dropped by
+// the hardware range check, so ragged M needs no per-row branches and every
+// load of a block can be in flight at once.  The lane's base offset covers its
+// row group and column slot; the row within the block travels in the scalar
+// offset.
+template <int MB, int N8, int W2, int NS, int EPI>
+struct Rows {
+    using Tile = RowTile<MB, N8, W2, NS>;
+    static constexpr int NT1 = Tile::NT1;
+    static constexpr int NT = Tile::NT;   // output columns a lane owns in one row
+    static constexpr int D = Tile::DCOV;
+
+    // Byte offset of (row mrow0 + 4g, column slot) in an [M][D] matrix of `elt`-byte values.
+    static __device__ __forceinline__ int off1(int mrow0, int g, int j, int elt) {
+        return ((mrow0 + 4 * g) * D + Tile::col1(j)) * elt;
+    }
+    static __device__ __forceinline__ int off2(int mrow0, int g, int j, int elt) {
+        return ((mrow0 + 4 * g) * D + Tile::col2(j)) * elt;
+    }
+    static constexpr int row_so(int mb, int r, int elt) { return (16 * mb + r) * D * elt; }
+
+    // The NT fp32 values this lane owns in each of the 4 rows of block mb.
+    static __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rs, int o1, int o2, int mb,
+                                                      float (&v)[4][NT]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int so = row_so(mb, r, 4);
+            if constexpr (N8 != 0) {
+                const f32x4_t x0 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, o1, so, 0));
+                const f32x4_t x1 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, o1 + 16, so, 0));
+#pragma unroll
+                for (int t = 0; t < 4; ++t) { v[r][t] = x0[t]; v[r][4 + t] = x1[t]; }
+            }
+            if constexpr (W2 == 2) {
+                const f32x2_t x = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, o2, so, 0));
+                v[r][NT1] = x[0]; v[r][NT1 + 1] = x[1];
+            }
+            if constexpr (W2 == 4) {
+                const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, o2, so, 0));
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[r][NT1 + t] = x[t];
+            }
+        }
+    }
+
+    // fp32 rows of block mb; AUX = kSc1 writes them through to memory.
+    template <int AUX>
+    static __device__ __forceinline__ void store_block_f32(__amdgpu_buffer_rsrc_t rs, int o1, int o2, int mb,
+                                                           const float (&v)[4][NT]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int so = row_so(mb, r, 4);
+            if constexpr (N8 != 0) {
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4_t, (f32x4_t){v[r][0], v[r][1], v[r][2], v[r][3]}), rs, o1, so, AUX);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4_t, (f32x4_t){v[r][4], v[r][5], v[r][6], v[r][7]}), rs, o1 + 16, so, AUX);
+            }
+            if constexpr (W2 == 2)
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, (f32x2_t){v[r][NT1], v[r][NT1 + 1]}),
+                                                      rs, o2, so, AUX);
+            if constexpr (W2 == 4)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4_t, (f32x4_t){v[r][NT1], v[r][NT1 + 1], v[r][NT1 + 2], v[r][NT1 + 3]}), rs,
+                    o2, so, AUX);
+        }
+    }
+
+    // bf16 rows of block mb (one rounding per element).
+    static __device__ __forceinline__ void store_block_bf16(__amdgpu_buffer_rsrc_t rs, int o1, int o2, int mb,
+                                                            const float (&v)[4][NT]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int so = row_so(mb, r, 2);
+            if constexpr (N8 != 0) {
+                const u32x4_t w = {pack_bf16x2(v[r][0], v[r][1]), pack_bf16x2(v[r][2], v[r][3]),
+                                   pack_bf16x2(v[r][4], v[r][5]), pack_bf16x2(v[r][6], v[r][7])};
+                __builtin_amdgcn_raw_buffer_store_b128(w, rs, o1, so, 0);
+            }
+            if constexpr (W2 == 2) __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(v[r][NT1], v[r][NT1 + 1]), rs, o2, so, 0);
+            if constexpr (W2 == 4) {
+                const u32x2_t w = {pack_bf16x2(v[r][NT1], v[r][NT1 + 1]), pack_bf16x2(v[r][NT1 + 2], v[r][NT1 + 3])};
+                __builtin_amdgcn_raw_buffer_store_b64(w, rs, o2, so, 0);
+            }
+        }
+    }
+
+    static __device__ __forceinline__ void tile_block(const Tile &T, int mb, float (&v)[4][NT]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) v[r][t] = T.acc[mb][t][r];
+    }
+
+    // Accumulators = the tile's rows of an fp32 [M][D] matrix.
+    static __device__ __forceinline__ void init_from(const RowArgs &a, Tile &T, const float *base, int mrow0, int g,
+                                                     int j) {
+        const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(base, a.M * D * 4);
+        const int o1 = off1(mrow0, g, j, 4), o2 = off2(mrow0, g, j, 4);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            float v[4][NT];
+            load_block(rs, o1, o2, mb, v);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) T.acc[mb][t][r] = v[r][t];
+        }
+    }
+
+    // Tile into an fp32 [M][D] matrix.
+    template <int AUX>
+    static __device__ __forceinline__ void store_f32(const RowArgs &a, const Tile &T, float *base, int mrow0, int g,
+                                                     int j) {
+        const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(base, a.M * D * 4);
+        const int o1 = off1(mrow0, g, j, 4), o2 = off2(mrow0, g, j, 4);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            float v[4][NT];
+            tile_block(T, mb, v);
+            store_block_f32<AUX>(rs, o1, o2, mb, v);
+        }
+    }
+
+    // Tile (+ an fp32 [M][D] matrix P when ADD) into a bf16 [M][D] matrix, block by
+    // block: a block's P loads are all in flight together, then its stores follow.
+    template <bool ADD>
+    static __device__ __forceinline__ void store_bf16(const RowArgs &a, const Tile &T, uint16_t *base,
+                                                      const float *pbase, int mrow0, int g, int j) {
+        const __amdgpu_buffer_rsrc_t ry = uniform_rsrc(base, a.M * D * 2);
+        const int y1 = off1(mrow0, g, j, 2), y2 = off2(mrow0, g, j, 2);
+        __amdgpu_buffer_rsrc_t rp;
+        int p1 = 0, p2 = 0;
+        if constexpr (ADD) {
+            rp = uniform_rsrc(pbase, a.M * D * 4);
+            p1 = off1(mrow0, g, j, 4);
+            p2 = off2(mrow0, g, j, 4);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            float v[4][NT];
+            if constexpr (ADD) {
+                load_block(rp, p1, p2, mb, v);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) v[r][t] += T.acc[mb][t][r];
+            } else {
+                tile_block(T, mb, v);
+            }
+            store_block_bf16(ry, y1, y2, mb, v);
+        }
+    }
+};
+
+// Bounded wait for a user flag to carry this launch's epoch (a timeout is
+// recorded and the wave goes on).  The asm keeps the caller's P_u loads after it.
+__device__ __forceinline__ void wait_flag(const RowArgs &a, const uint32_t *f, int lane) {
+    uint32_t polls = 0;
+    while (__builtin_amdgcn_readfirstlane(ld_flag(f)) != a.epoch) {
+        if (++polls >= a.spin_limit) {
+            if (lane == 0) atomicOr(a.err, ERRBIT_TIMEOUT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
+constexpr int kRing = 4;   // K steps in the register ring (three in flight while one multiplies)
+
+template <int MB, int N8, int W2, int EPI>
+__global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
+    using R = Rows<MB, N8, W2, kRing, EPI>;
+    using Tile = typename R::Tile;
+    extern __shared__ __align__(16) uint16_t lds[];
+
+    const int wpb = (int)(blockDim.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, j = lane & 15;
+    const int n_mc = a.n_mchunks;
+    const int n_total = a.n_user + a.n_cand;
+    const int n_waves = (int)gridDim.x * wpb;
+    const int first = (int)__builtin_amdgcn_readfirstlane(blockIdx.x * wpb + (threadIdx.x >> 6));
+    const int D = Tile::DCOV;
+
+    auto rsrc_of = [&](int t) {
+        if (t >= n_total) return uniform_rsrc(nullptr, 0);
+        if (t < a.n_user) return uniform_rsrc(a.U + (size_t)(t / n_mc) * a.K_u * D, a.K_u * D * 2);
+        return uniform_rsrc(a.C + (size_t)((t - a.n_user) / n_mc) * a.K_c * D, a.K_c * D * 2);
+    };
+
+    Tile T;
+    T.init(g, j);
+    int t = first;
+    __amdgpu_buffer_rsrc_t rs = rsrc_of(t);
+
+    // ---- stage the projections.  LDS: [W_c if candidates run][W_u if users run], each
+    // lds_w_elems(M, K) elements.  The first unit's opening steps go out right behind the
+    // first projection loads, so their memory latency overlaps the staging.
+    uint16_t *wl_c = lds;
+    uint16_t *wl_u = lds + (a.n_cand > 0 ? lds_w_elems(a.M, a.K_wc) : 0);
+    const bool need_u = (int)blockIdx.x * wpb < a.n_user;   // user units are the first unit of waves 0..n_user-1
+    auto prologue = [&]() { T.prologue(rs); };
+    if (a.n_cand > 0) {
+        stage_flat(a.W_c, a.M * a.K_wc, wl_c, prologue);
+        if (need_u) stage_flat(a.W_u, a.M * a.K_u, wl_u, [] {});
+    } else if (need_u) {
+        stage_flat(a.W_u, a.M * a.K_u, wl_u, prologue);
+    } else {
+        prologue();
+    }
+    __syncthreads();
+    if (first >= n_total) return;
+
+    for (;;) {
+        t = (int)__builtin_amdgcn_readfirstlane(t);
+        const int tn = t + n_waves;
+        const __amdgpu_buffer_rsrc_t rs_next = rsrc_of(tn);
+        T.zero();
+        if (t < a.n_user) {
+            // ---- user unit (u, mc) ----
+            const int mc = t % n_mc;
+            const int u = t / n_mc;
+            const int mrow0 = mc * MB * 16;
+            T.run(rs, rs_next, a.n_ks_u, wl_u, a.K_u, a.M, mrow0, g, j);
+            if (!(a.debug_flags & 4u)) {                        // IKBO_FLAG_DEBUG_SKIP_USER: never publish
+                R::template store_f32<kSc1>(a, T, a.P_u + (size_t)u * a.M * D, mrow0, g, j);
+                if (a.wait_flags) {
+                    if (a.debug_flags & 2u)                     // IKBO_FLAG_DEBUG_DELAY_USER
+                        for (int i = 0; i < 64; ++i) __builtin_amdgcn_s_sleep(127);
+                    wait_stores();
+                    if (lane == 0) st_flag(&a.flags[2 + u * n_mc + mc], a.epoch);
+                }
+            }
+        } else {
+            // ---- candidate unit (b, mc) ----
+            const int c = t - a.n_user;
+            const int mc = c % n_mc;
+            const int b = c / n_mc;
+            const int mrow0 = mc * MB * 16;
+            const size_t obase = (size_t)b * a.M * D;
+            if constexpr (EPI == EPI_ADD_USER) {
+                // Rows of P_u[map[b]] are added either by starting the accumulators from
+                // them (the wave's later units, when the user product is in place before
+                // the unit starts) or in the epilogue (a wave's first unit of a launch that
+                // also computes the users, so that it never waits on them up front).  The
+                // choice depends only on the unit's place in the schedule, so results do
+                // not depend on timing.
+                const int u = (int)__builtin_amdgcn_readfirstlane(a.map[b]);
+                const bool valid = u >= 0 && u < a.B_u;
+                const bool pre = valid && (!a.wait_flags || t >= n_waves);
+                const float *pu = a.P_u + (size_t)(valid ? u : 0) * a.M * D;
+                const uint32_t *flag = &a.flags[2 + (valid ? u : 0) * n_mc + mc];
+                if (pre) {
+                    if (a.wait_flags) wait_flag(a, flag, lane);
+                    R::init_from(a, T, pu, mrow0, g, j);
+                }
+                T.run(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
+                uint16_t *y = static_cast<uint16_t *>(a.out) + obase;
+                if (!valid) {
+                    if (lane == 0) atomicOr(a.err, ERRBIT_MAP);
+                } else if (pre) {
+                    R::template store_bf16<false>(a, T, y, nullptr, mrow0, g, j);
+                } else {
+                    if (a.wait_flags) wait_flag(a, flag, lane);
+                    R::template store_bf16<true>(a, T, y, pu, mrow0, g, j);
+                }
+            } else {
+                T.run(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
+                if constexpr (EPI == EPI_STORE_F32)
+                    R::template store_f32<0>(a, T, static_cast<float *>(a.out) + obase, mrow0, g, j);
+                else
+                    R::template store_bf16<false>(a, T, static_cast<uint16_t *>(a.out) + obase, nullptr, mrow0, g,
+                                                  j);
+            }
+        }
+        if (tn >= n_total) break;
+        t = tn;
+        rs = rs_next;
+    }
+}
+
+typedef void (*rows_kernel_t)(RowArgs);
+
+template <int N8, int W2, int EPI>
+rows_kernel_t pick_mb(int mb) {
+    switch (mb) {
+        case 1: return lce_rows_kernel<1, N8, W2, EPI>;
+        case 2: return lce_rows_kernel<2, N8, W2, EPI>;
+        case 3: return lce_rows_kernel<3, N8, W2, EPI>;
+        case 4: return lce_rows_kernel<4, N8, W2, EPI>;
+    }
+    return nullptr;
+}
+
+template <int EPI>
+rows_kernel_t pick_layout(int D, int mb) {
+    switch (D) {
+        case 160: return pick_mb<1, 2, EPI>(mb);
+        case 128: return pick_mb<1, 0, EPI>(mb);
+        case 192: return pick_mb<1, 4, EPI>(mb);
+        case 64: return pick_mb<0, 4, EPI>(mb);
+        case 32: return pick_mb<0, 2, EPI>(mb);
+    }
+    return nullptr;
+}
+
+rows_kernel_t pick(int epi, int D, int mb) {
+    switch (epi) {
+        case EPI_STORE_F32: return pick_layout<EPI_STORE_F32>(D, mb);
+        case EPI_ADD_USER: return pick_layout<EPI_ADD_USER>(D, mb);
+        case EPI_STORE_T: return pick_layout<EPI_STORE_T>(D, mb);
+    }
+    return nullptr;
+}
+
+}  // namespace
+
+bool rows_supported(int D) { return D == 160 || D == 128 || D == 192 || D == 64 || D == 32; }
+
+int rows_max_mb(int D) {
+    // Accumulators per lane = 4 * MB * (columns per lane): keep them at or below 128.
+    const int nt = (D >= 128 ? 8 : 0) + (D % 128) / 16;
+    int mb = 32 / (nt > 0 ? nt : 1);
+    return mb < 1 ? 1 : (mb > 4 ? 4 : mb);
+}
+
+size_t rows_lds_bytes(const RowArgs &a) {
+    size_t b = 0;
+    if (a.n_cand > 0) b += (size_t)lds_w_elems(a.M, a.K_wc) * 2;
+    if (a.n_user > 0) b += (size_t)lds_w_elems(a.M, a.K_u) * 2;
+    return b;
+}
+
+int rows_blocks_per_cu(int epi, int D, int mb, size_t lds_bytes) {
+    rows_kernel_t k = pick(epi, D, mb);
+    if (k == nullptr) return 0;
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds_bytes) != hipSuccess)
+        return 0;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(k), kRowsBlock,
+                                                     lds_bytes) != hipSuccess)
+        return 0;
+    return n;
+}
+
+hipError_t launch_rows(int epi, int mb, const RowArgs &a, int grid, hipStream_t s) {
+    rows_kernel_t k = pick(epi, a.D, mb);
+    if (k == nullptr || grid < 1) return hipErrorInvalidValue;
+    const size_t lds = rows_lds_bytes(a);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    RowArgs args = a;
+    void *params[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void *>(k), dim3(grid), dim3(kRowsBlock), params, lds, s);
+}
+
+}  // namespace ikbo

@@ -12,8 +12,6 @@
 
 namespace ikbo {
 
-__device__ __forceinline__ int imin_t(int a, int b) { return a < b ? a : b; }
-
 // A operand (one lane): W[m][k .. k+7] as 8 bf16 values.
 template <bool PACKED>
 __device__ __forceinline__ u32x4_t load_a_bf16(const uint16_t *__restrict__ W, int ldw, int M, int K,
