@@ -135,8 +135,8 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     if (e != hipSuccess) { delete p; return hip_fail(e, "hipDeviceGetAttribute(CUs)"); }
     int max_lds = 0;
     e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, p->device);
-    p->max_lds = max_lds;
     if (e != hipSuccess) { delete p; return hip_fail(e, "hipDeviceGetAttribute(LDS)"); }
+    p->max_lds = max_lds;
 
     const int n_mblocks = ceil_div(M, 16);
     p->n_mblocks = n_mblocks;

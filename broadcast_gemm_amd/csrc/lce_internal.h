@@ -132,8 +132,7 @@ struct RowArgs {
 
 bool rows_supported(int D);
 int rows_max_mb(int D);
-size_t rows_tile_bytes(const RowArgs &a);
-size_t rows_lds_bytes(const RowArgs &a);
+size_t rows_lds_bytes(const RowArgs &a);   // dynamic LDS of one launch (staged projections)
 int rows_blocks_per_cu(int epi, int D, int mb, size_t lds_bytes);
 hipError_t launch_rows(int epi, int mb, const RowArgs &a, int grid, hipStream_t s);
 

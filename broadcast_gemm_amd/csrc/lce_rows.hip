@@ -3,17 +3,16 @@
 // One kernel template serves the ladder stages that decompose the product (and
 // the materialised baseline).  A workgroup of four waves (one per SIMD, so each
 // wave may hold 512 registers) stages the projections it needs in LDS once, then
-// every wave works through a static list of units, wave w taking units w, w + T,
-// w + 2T, ... (T = waves in the grid).  Units are numbered
+// every wave works through a static list of units:
 //
-//   user units      [0, n_user): (u, mc) = rows [mc*16*MB, +16*MB) of
+//   user units      t in [0, n_user): (u, mc) = rows [mc*16*MB, +16*MB) of
 //                   P_u[u] = W_u . U[u] in fp32 (IKBO recsys blog, "Deep Dive:
 //                   Linear Compression", stage 1: the user product at its own
 //                   batch size);
-//   candidate units [n_user, n_user + n_cand): (b, mc) = rows of W_c . C[b]; the
-//                   epilogue stores fp32 (unfused ladder stages), stores bf16
-//                   (baseline), or gathers P_u[map[b]] by index, adds it in
-//                   registers and stores Y once (stage 3), first waiting for flag
+//   candidate units c in [0, n_cand): (b, mc) = rows of W_c . C[b]; the epilogue
+//                   stores fp32 (unfused ladder stages), stores bf16 (baseline),
+//                   or adds the rows of P_u[map[b]] gathered by index in
+//                   registers and stores Y once (stage 3), waiting for flag
 //                   (map[b], mc) when the user units run in the same launch
 //                   (stage 4: one launch, user and candidate work overlapped).
 //
@@ -29,11 +28,13 @@
 // hold an older copy.  Agent-scope fences would instead write back or
 // invalidate a whole L2 per use.
 //
-// There is no device-wide work counter: a single hot atomic serialises every
-// wave of the grid.  The host sizes the grid to be co-resident and guarantees
-// n_user <= T, so every user unit is the first unit of its wave and never sits
-// behind a wait; every poll is also bounded (a timeout is recorded and the wave
-// moves on).  The epoch is supplied per launch by the host.
+// There is no device-wide work counter: contended atomics on one address
+// serialise at about 12 ns each, more than the whole schedule is worth.  The
+// host sizes the grid to be co-resident and guarantees n_user <= T (waves in
+// the grid) when both kinds share a launch, so every user unit is the first unit
+// of its wave and never sits behind a wait; every poll is also bounded (a
+// timeout is recorded and the wave moves on).  The epoch is supplied per launch
+// by the host.
 #include <algorithm>
 
 #include "lce_internal.h"
@@ -50,6 +51,7 @@ __device__ __forceinline__ void st_flag(uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 constexpr int kSc1 = 16;   // buffer cache-policy bit sc1: device scope (write through this XCD's L2)
+constexpr int kNt = 2;     // buffer cache-policy bit nt: non-temporal (streaming) stores
 
 // Wait until every store this wave issued has been acknowledged.  Stores made
 // with kSc1 are then visible to every XCD, and a flag or counter update issued
@@ -126,7 +128,8 @@ struct Rows {
         }
     }
 
-    // bf16 rows of block mb (one rounding per element).
+    // bf16 rows of block mb (one rounding per element).  Y is written with the
+    // non-temporal (streaming) policy: the launch never reads it back.
     static __device__ __forceinline__ void store_block_bf16(__amdgpu_buffer_rsrc_t rs, int o1, int o2, int mb,
                                                             const float (&v)[4][NT]) {
 #pragma unroll
@@ -135,12 +138,12 @@ struct Rows {
             if constexpr (N8 != 0) {
                 const u32x4_t w = {pack_bf16x2(v[r][0], v[r][1]), pack_bf16x2(v[r][2], v[r][3]),
                                    pack_bf16x2(v[r][4], v[r][5]), pack_bf16x2(v[r][6], v[r][7])};
-                __builtin_amdgcn_raw_buffer_store_b128(w, rs, o1, so, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(w, rs, o1, so, kNt);
             }
-            if constexpr (W2 == 2) __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(v[r][NT1], v[r][NT1 + 1]), rs, o2, so, 0);
+            if constexpr (W2 == 2) __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(v[r][NT1], v[r][NT1 + 1]), rs, o2, so, kNt);
             if constexpr (W2 == 4) {
                 const u32x2_t w = {pack_bf16x2(v[r][NT1], v[r][NT1 + 1]), pack_bf16x2(v[r][NT1 + 2], v[r][NT1 + 3])};
-                __builtin_amdgcn_raw_buffer_store_b64(w, rs, o2, so, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(w, rs, o2, so, kNt);
             }
         }
     }
@@ -233,110 +236,138 @@ template <int MB, int N8, int W2, int EPI>
 __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     using R = Rows<MB, N8, W2, kRing, EPI>;
     using Tile = typename R::Tile;
-    extern __shared__ __align__(16) uint16_t lds[];
 
     const int wpb = (int)(blockDim.x >> 6);
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, j = lane & 15;
     const int n_mc = a.n_mchunks;
-    const int n_total = a.n_user + a.n_cand;
     const int n_waves = (int)gridDim.x * wpb;
     const int first = (int)__builtin_amdgcn_readfirstlane(blockIdx.x * wpb + (threadIdx.x >> 6));
     const int D = Tile::DCOV;
 
-    auto rsrc_of = [&](int t) {
-        if (t >= n_total) return uniform_rsrc(nullptr, 0);
-        if (t < a.n_user) return uniform_rsrc(a.U + (size_t)(t / n_mc) * a.K_u * D, a.K_u * D * 2);
-        return uniform_rsrc(a.C + (size_t)((t - a.n_user) / n_mc) * a.K_c * D, a.K_c * D * 2);
+    // ---- schedule (static, every value wave-uniform) ----
+    // User units t in [0, n_user): wave w takes t = w, w + T, ...  In a launch with both kinds
+    // the host guarantees n_user <= T, so a user unit is always a wave's first unit.
+    // Candidate units: round 0 goes to the waves without a user unit, later rounds to every
+    // wave; within a round waves are taken in reverse order, so a partial last round lands
+    // on waves that did no user work.
+    const int w = first;
+    const bool both = a.n_user > 0 && a.n_cand > 0;
+    const int nuw = both ? imin_t(a.n_user, n_waves) : 0;   // waves whose first unit is a user unit
+    const int V = n_waves - nuw;
+    const int wr = n_waves - 1 - w;
+    auto cand_of = [&](int k) {   // k-th candidate unit of this wave (n_cand when none)
+        const int c = w >= nuw ? (k == 0 ? wr : V + (k - 1) * n_waves + wr) : V + k * n_waves + wr;
+        return c < a.n_cand ? c : a.n_cand;
+    };
+    auto user_rsrc = [&](int t) {
+        return t < a.n_user ? uniform_rsrc(a.U + (size_t)(t / n_mc) * a.K_u * D, a.K_u * D * 2)
+                            : uniform_rsrc(nullptr, 0);
+    };
+    auto cand_rsrc = [&](int c) {
+        return c < a.n_cand ? uniform_rsrc(a.C + (size_t)(c / n_mc) * a.K_c * D, a.K_c * D * 2)
+                            : uniform_rsrc(nullptr, 0);
     };
 
     Tile T;
     T.init(g, j);
-    int t = first;
-    __amdgpu_buffer_rsrc_t rs = rsrc_of(t);
+    int t = w;                     // current user unit
+    int kc = 0;                    // index of the current candidate unit in this wave's list
+    int c = cand_of(0);
+    __amdgpu_buffer_rsrc_t rs = t < a.n_user ? user_rsrc(t) : cand_rsrc(c);
 
     // ---- stage the projections.  LDS: [W_c if candidates run][W_u if users run], each
-    // lds_w_elems(M, K) elements.  The first unit's opening steps go out right behind the
-    // first projection loads, so their memory latency overlaps the staging.
+    // lds_w_elems(M, K) elements, copied as is.  The first unit's opening steps go out
+    // right behind the first projection loads, so their memory latency overlaps the
+    // staging.  Blocks that hold user units of a launch with both kinds stage W_u first
+    // and W_c only after their user units, so that the user products (which candidates
+    // wait for) start early.
+    extern __shared__ __align__(16) uint16_t lds[];
     uint16_t *wl_c = lds;
     uint16_t *wl_u = lds + (a.n_cand > 0 ? lds_w_elems(a.M, a.K_wc) : 0);
-    const bool need_u = (int)blockIdx.x * wpb < a.n_user;   // user units are the first unit of waves 0..n_user-1
+    const bool need_u = (int)blockIdx.x * wpb < a.n_user;   // this block holds user units
     auto prologue = [&]() { T.prologue(rs); };
-    if (a.n_cand > 0) {
-        stage_flat(a.W_c, a.M * a.K_wc, wl_c, prologue);
-        if (need_u) stage_flat(a.W_u, a.M * a.K_u, wl_u, [] {});
-    } else if (need_u) {
+    if (need_u)
         stage_flat(a.W_u, a.M * a.K_u, wl_u, prologue);
-    } else {
+    else if (a.n_cand > 0)
+        stage_flat(a.W_c, a.M * a.K_wc, wl_c, prologue);
+    else
         prologue();
-    }
     __syncthreads();
-    if (first >= n_total) return;
 
-    for (;;) {
+    // ---- user units ----
+    while (t < a.n_user) {
         t = (int)__builtin_amdgcn_readfirstlane(t);
         const int tn = t + n_waves;
-        const __amdgpu_buffer_rsrc_t rs_next = rsrc_of(tn);
+        const __amdgpu_buffer_rsrc_t rs_next = tn < a.n_user ? user_rsrc(tn) : cand_rsrc(c);
+        const int mc = t % n_mc;
+        const int u = t / n_mc;
+        const int mrow0 = mc * MB * 16;
         T.zero();
-        if (t < a.n_user) {
-            // ---- user unit (u, mc) ----
-            const int mc = t % n_mc;
-            const int u = t / n_mc;
-            const int mrow0 = mc * MB * 16;
-            T.run(rs, rs_next, a.n_ks_u, wl_u, a.K_u, a.M, mrow0, g, j);
-            if (!(a.debug_flags & 4u)) {                        // IKBO_FLAG_DEBUG_SKIP_USER: never publish
-                R::template store_f32<kSc1>(a, T, a.P_u + (size_t)u * a.M * D, mrow0, g, j);
-                if (a.wait_flags) {
-                    if (a.debug_flags & 2u)                     // IKBO_FLAG_DEBUG_DELAY_USER
-                        for (int i = 0; i < 64; ++i) __builtin_amdgcn_s_sleep(127);
-                    wait_stores();
-                    if (lane == 0) st_flag(&a.flags[2 + u * n_mc + mc], a.epoch);
-                }
-            }
-        } else {
-            // ---- candidate unit (b, mc) ----
-            const int c = t - a.n_user;
-            const int mc = c % n_mc;
-            const int b = c / n_mc;
-            const int mrow0 = mc * MB * 16;
-            const size_t obase = (size_t)b * a.M * D;
-            if constexpr (EPI == EPI_ADD_USER) {
-                // Rows of P_u[map[b]] are added either by starting the accumulators from
-                // them (the wave's later units, when the user product is in place before
-                // the unit starts) or in the epilogue (a wave's first unit of a launch that
-                // also computes the users, so that it never waits on them up front).  The
-                // choice depends only on the unit's place in the schedule, so results do
-                // not depend on timing.
-                const int u = (int)__builtin_amdgcn_readfirstlane(a.map[b]);
-                const bool valid = u >= 0 && u < a.B_u;
-                const bool pre = valid && (!a.wait_flags || t >= n_waves);
-                const float *pu = a.P_u + (size_t)(valid ? u : 0) * a.M * D;
-                const uint32_t *flag = &a.flags[2 + (valid ? u : 0) * n_mc + mc];
-                if (pre) {
-                    if (a.wait_flags) wait_flag(a, flag, lane);
-                    R::init_from(a, T, pu, mrow0, g, j);
-                }
-                T.run(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
-                uint16_t *y = static_cast<uint16_t *>(a.out) + obase;
-                if (!valid) {
-                    if (lane == 0) atomicOr(a.err, ERRBIT_MAP);
-                } else if (pre) {
-                    R::template store_bf16<false>(a, T, y, nullptr, mrow0, g, j);
-                } else {
-                    if (a.wait_flags) wait_flag(a, flag, lane);
-                    R::template store_bf16<true>(a, T, y, pu, mrow0, g, j);
-                }
-            } else {
-                T.run(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
-                if constexpr (EPI == EPI_STORE_F32)
-                    R::template store_f32<0>(a, T, static_cast<float *>(a.out) + obase, mrow0, g, j);
-                else
-                    R::template store_bf16<false>(a, T, static_cast<uint16_t *>(a.out) + obase, nullptr, mrow0, g,
-                                                  j);
+        T.run(rs, rs_next, a.n_ks_u, wl_u, a.K_u, a.M, mrow0, g, j);
+        if (!(a.debug_flags & 4u)) {                        // IKBO_FLAG_DEBUG_SKIP_USER: never publish
+            R::template store_f32<kSc1>(a, T, a.P_u + (size_t)u * a.M * D, mrow0, g, j);
+            if (a.wait_flags) {
+                if (a.debug_flags & 2u)                     // IKBO_FLAG_DEBUG_DELAY_USER
+                    for (int i = 0; i < 64; ++i) __builtin_amdgcn_s_sleep(127);
+                wait_stores();
+                if (lane == 0) st_flag(&a.flags[2 + u * n_mc + mc], a.epoch);
             }
         }
-        if (tn >= n_total) break;
         t = tn;
+        rs = rs_next;
+    }
+    if (need_u && both) {
+        // The ring already holds the first candidate unit's opening steps.
+        stage_flat(a.W_c, a.M * a.K_wc, wl_c, [] {});
+        __syncthreads();
+    }
+
+    // ---- candidate units (b, mc) ----
+    while (c < a.n_cand) {
+        c = (int)__builtin_amdgcn_readfirstlane(c);
+        const int cn = cand_of(kc + 1);
+        const __amdgpu_buffer_rsrc_t rs_next = cand_rsrc(cn);
+        const int mc = c % n_mc;
+        const int b = c / n_mc;
+        const int mrow0 = mc * MB * 16;
+        const size_t obase = (size_t)b * a.M * D;
+        T.zero();
+        if constexpr (EPI == EPI_ADD_USER) {
+            // Rows of P_u[map[b]] are added either by starting the accumulators from them
+            // (when the user product is known to be in place before the unit starts: a launch
+            // without user units, or a wave's later candidate units) or in the epilogue (a
+            // wave's first candidate unit in a launch that also computes the users, so that it
+            // never waits on them up front).  The choice depends only on the schedule, so
+            // results do not depend on timing.
+            const int u = (int)__builtin_amdgcn_readfirstlane(a.map[b]);
+            const bool valid = u >= 0 && u < a.B_u;
+            const bool pre = valid && (!a.wait_flags || kc > 0);
+            const float *pu = a.P_u + (size_t)(valid ? u : 0) * a.M * D;
+            const uint32_t *flag = &a.flags[2 + (valid ? u : 0) * n_mc + mc];
+            if (pre) {
+                if (a.wait_flags) wait_flag(a, flag, lane);
+                R::init_from(a, T, pu, mrow0, g, j);
+            }
+            T.run(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
+            uint16_t *y = static_cast<uint16_t *>(a.out) + obase;
+            if (!valid) {
+                if (lane == 0) atomicOr(a.err, ERRBIT_MAP);
+            } else if (pre) {
+                R::template store_bf16<false>(a, T, y, nullptr, mrow0, g, j);
+            } else {
+                if (a.wait_flags) wait_flag(a, flag, lane);
+                R::template store_bf16<true>(a, T, y, pu, mrow0, g, j);
+            }
+        } else {
+            T.run(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
+            if constexpr (EPI == EPI_STORE_F32)
+                R::template store_f32<0>(a, T, static_cast<float *>(a.out) + obase, mrow0, g, j);
+            else
+                R::template store_bf16<false>(a, T, static_cast<uint16_t *>(a.out) + obase, nullptr, mrow0, g, j);
+        }
+        c = cn;
+        ++kc;
         rs = rs_next;
     }
 }

@@ -56,10 +56,22 @@ def cached_oracle(name: str):
     return oracle.lce_f64(x.U, x.C, x.map, x.W_u, x.W_c, rows=rows), rows
 
 
+def mismatch_pattern(Y_gpu: np.ndarray, Y_ref: np.ndarray) -> str:
+    """Where the elements outside tolerance sit (batch entries, rows mod 16, 8-column slots)."""
+    bad = np.abs(Y_gpu - Y_ref) > ATOL + RTOL * np.abs(Y_ref)
+    if Y_ref.ndim != 3 or not bad.any():
+        return ""
+    b, m, d = np.nonzero(bad)
+    ub = np.unique(b)
+    return (f"; entries {len(ub)} (first {ub[:8].tolist()}), rows%16 {np.bincount(m % 16, minlength=16).tolist()}, "
+            f"row blocks {np.bincount(m // 16).tolist()}, column slots {np.bincount(d // 8).tolist()}")
+
+
 def assert_close(Y_gpu: np.ndarray, Y_ref: np.ndarray, what: str):
     import oracle
     nbad, excess = oracle.tolerance_violations(Y_gpu, Y_ref, ATOL, RTOL)
-    assert nbad == 0, f"{what}: {nbad} of {Y_ref.size} elements outside tolerance (max excess {excess:.3g})"
+    assert nbad == 0, (f"{what}: {nbad} of {Y_ref.size} elements outside tolerance (max excess {excess:.3g})"
+                       + mismatch_pattern(Y_gpu, Y_ref))
 
 
 CONFIG_NAMES = [c.name for c in CONFIGS]
