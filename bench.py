@@ -95,6 +95,58 @@ def cpu_baseline(cfg, x, min_seconds: float, max_reps: int):
                       f"{el:.1f} s wall", "seconds_per_forward": round(el / reps, 4)}
 
 
+def _counter_rows(d: str, counter: str):
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter:
+                    rows.append(r)
+    return rows
+
+
+def _mean_kib(d: str, counter: str, match: str) -> tuple:
+    vals = [float(r["Counter_Value"]) for r in _counter_rows(d, counter) if match in r.get("Kernel_Name", "")]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {match!r} under {d}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def run_traffic(args) -> int:
+    """Write profiles/traffic_<workload>_<variant>.json from four rocprofv3 --pmc runs (no GPU).
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the forward kernel are scaled by what
+    the same counters read for a plain device copy of known size."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic
+    copy_bytes = args.copy_mib << 20
+    f_kib, nf = _mean_kib(fetch_dir, "FETCH_SIZE", args.kernel_match)
+    w_kib, nw = _mean_kib(write_dir, "WRITE_SIZE", args.kernel_match)
+    cf_kib, _ = _mean_kib(cfetch_dir, "FETCH_SIZE", args.copy_match)
+    cw_kib, _ = _mean_kib(cwrite_dir, "WRITE_SIZE", args.copy_match)
+    kf = copy_bytes / (cf_kib * 1024.0)
+    kw = copy_bytes / (cw_kib * 1024.0)
+    fetch_b = f_kib * 1024.0 * kf
+    write_b = w_kib * 1024.0 * kw
+    from broadcast_gemm_amd.inputs import CONFIG_BY_NAME
+    cfg = CONFIG_BY_NAME[args.config]
+    out = {"workload": cfg.name, "variant": args.variant, "kernel_match": args.kernel_match,
+           "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
+           "dispatches": [nf, nw], "copy_bytes": copy_bytes,
+           "copy_fetch_kib": round(cf_kib, 1), "copy_write_kib": round(cw_kib, 1),
+           "scale_fetch": round(kf, 4), "scale_write": round(kw, 4),
+           "hbm_fetch_bytes_per_launch": round(fetch_b), "hbm_write_bytes_per_launch": round(write_b),
+           "hbm_bytes_per_launch": round(fetch_b + write_b),
+           "algorithmic_bytes": algorithmic_bytes(cfg), "kernel_source_hash": kernel_source_hash()}
+    path = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}_{args.variant}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def run_copy(args) -> int:
     """Plain device copy of known size (calibrates FETCH_SIZE/WRITE_SIZE counters)."""
     import torch
@@ -118,9 +170,15 @@ def main() -> int:
     ap.add_argument("--rotate-mb", type=int, default=1100, help="total size of rotated buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--mode", default="lce", choices=["lce", "copy"])
+    ap.add_argument("--mode", default="lce", choices=["lce", "copy", "traffic"])
     ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="--mode traffic: rocprofv3 --pmc output directories")
+    ap.add_argument("--kernel-match", default="lce_rows_kernel")
+    ap.add_argument("--copy-match", default="copyBuffer")
     args = ap.parse_args()
+    if args.mode == "traffic":
+        return run_traffic(args)
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the IKBO LCE forward needs no collective, and "
