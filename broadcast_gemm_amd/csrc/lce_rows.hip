@@ -324,6 +324,40 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     }
 
     // ---- candidate units (b, mc) ----
+    // Gather-add epilogue after waiting for the user flag (bounded): Y = tile + P_u[map[b]].
+    auto add_user_store = [&](const Tile &X, int cc) {
+        const int mc = cc % n_mc;
+        const int b = cc / n_mc;
+        const int u = (int)__builtin_amdgcn_readfirstlane(a.map[b]);
+        if (u < 0 || u >= a.B_u) {
+            if (lane == 0) atomicOr(a.err, ERRBIT_MAP);
+            return;
+        }
+        if (a.wait_flags) wait_flag(a, &a.flags[2 + u * n_mc + mc], lane);
+        R::template store_bf16<true>(a, X, static_cast<uint16_t *>(a.out) + (size_t)b * a.M * D,
+                                     a.P_u + (size_t)u * a.M * D, mc * MB * 16, g, j);
+    };
+    if constexpr (EPI == EPI_ADD_USER) {
+        if (a.wait_flags && c < a.n_cand) {
+            // With the users in the same launch, a wave's first two candidate units run their K
+            // loops back to back (two sets of accumulators) before either epilogue, so the first
+            // wait for a user product comes after two units' worth of reads.
+            const int c1 = cand_of(1), c2 = cand_of(2);
+            const __amdgpu_buffer_rsrc_t rs1 = cand_rsrc(c1), rs2 = cand_rsrc(c2);
+            T.zero();
+            T.run(rs, rs1, a.n_ks_c, wl_c, a.K_wc, a.M, (c % n_mc) * MB * 16, g, j);
+            const Tile T0 = T;
+            if (c1 < a.n_cand) {
+                T.zero();
+                T.run(rs1, rs2, a.n_ks_c, wl_c, a.K_wc, a.M, (c1 % n_mc) * MB * 16, g, j);
+            }
+            add_user_store(T0, c);
+            if (c1 < a.n_cand) add_user_store(T, c1);
+            c = c2;
+            kc = 2;
+            rs = rs2;
+        }
+    }
     while (c < a.n_cand) {
         c = (int)__builtin_amdgcn_readfirstlane(c);
         const int cn = cand_of(kc + 1);
@@ -334,31 +368,19 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         const size_t obase = (size_t)b * a.M * D;
         T.zero();
         if constexpr (EPI == EPI_ADD_USER) {
-            // Rows of P_u[map[b]] are added either by starting the accumulators from them
-            // (when the user product is known to be in place before the unit starts: a launch
-            // without user units, or a wave's later candidate units) or in the epilogue (a
-            // wave's first candidate unit in a launch that also computes the users, so that it
-            // never waits on them up front).  The choice depends only on the schedule, so
-            // results do not depend on timing.
+            // Later units start their accumulators from the rows of P_u[map[b]] (in place by
+            // then: a launch without user units, or after the wave's first two units).
             const int u = (int)__builtin_amdgcn_readfirstlane(a.map[b]);
             const bool valid = u >= 0 && u < a.B_u;
-            const bool pre = valid && (!a.wait_flags || kc > 0);
-            const float *pu = a.P_u + (size_t)(valid ? u : 0) * a.M * D;
-            const uint32_t *flag = &a.flags[2 + (valid ? u : 0) * n_mc + mc];
-            if (pre) {
-                if (a.wait_flags) wait_flag(a, flag, lane);
-                R::init_from(a, T, pu, mrow0, g, j);
+            if (valid) {
+                if (a.wait_flags) wait_flag(a, &a.flags[2 + u * n_mc + mc], lane);
+                R::init_from(a, T, a.P_u + (size_t)u * a.M * D, mrow0, g, j);
             }
             T.run(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
-            uint16_t *y = static_cast<uint16_t *>(a.out) + obase;
-            if (!valid) {
-                if (lane == 0) atomicOr(a.err, ERRBIT_MAP);
-            } else if (pre) {
-                R::template store_bf16<false>(a, T, y, nullptr, mrow0, g, j);
-            } else {
-                if (a.wait_flags) wait_flag(a, flag, lane);
-                R::template store_bf16<true>(a, T, y, pu, mrow0, g, j);
-            }
+            if (valid)
+                R::template store_bf16<false>(a, T, static_cast<uint16_t *>(a.out) + obase, nullptr, mrow0, g, j);
+            else if (lane == 0)
+                atomicOr(a.err, ERRBIT_MAP);
         } else {
             T.run(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
             if constexpr (EPI == EPI_STORE_F32)
