@@ -196,7 +196,7 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     const size_t pc_bytes = (size_t)max_B_c * M * D * 4;
     const size_t n_units = (size_t)std::max(p->n_ucols_max, max_B_u) * p->n_mchunks;
     const size_t o_ctr = take(n_units * 4);
-    const size_t o_flag = take((n_units + 2 + 2 * (size_t)p->n_mchunks) * 4);
+    const size_t o_flag = take((std::max(n_units, (size_t)max_B_u * n_mblocks) + 2 + 2 * (size_t)p->n_mchunks) * 4);
     size_t o_wu = 0, o_wc = 0, o_wcat = 0, o_x = 0, o_pu = 0, o_pc = 0, o_pb = 0, o_part = 0;
     const bool flat = p->engine == ENGINE_FLAT;
     if (variant == IKBO_S0_MATERIALISED) {
@@ -358,9 +358,10 @@ int forward_rows(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t 
     a.K_u = K_u; a.K_c = K_c; a.K_wc = K_c;
     a.n_ks_u = ceil_div(K_u, 32); a.n_ks_c = ceil_div(K_c, 32);
     a.n_mchunks = p->n_mchunks;
+    a.n_mblocks = p->n_mblocks;
     a.spin_limit = p->spin_limit;
     a.debug_flags = p->flags;
-    const int n_user = B_u * p->n_mchunks;
+    const int n_user = B_u * p->n_mblocks;
     const int n_cand = B_c * p->n_mchunks;
     hipError_t e;
     switch (p->variant) {

@@ -117,13 +117,14 @@ struct RowArgs {
     const int32_t *map;
     void *out;                    // Y (bf16) or P_c (fp32)
     float *P_u;                   // [B_u][M][D]
-    uint32_t *flags;              // [2 + B_u * n_mchunks] user flags (epochs) from index 2
+    uint32_t *flags;              // [2 + B_u * n_mblocks] user flags (epochs) from index 2
     uint32_t *err;
     uint32_t epoch;               // value user units publish and candidates wait for
     int B_u, M, D, M_pad;
     int K_u, K_c, K_wc;           // K_c: rows of C[b]; K_wc >= K_c: row length of W_c (zero past K_c)
     int n_ks_u, n_ks_c;
-    int n_mchunks;
+    int n_mchunks;                // candidate units per entry (16*MB rows each)
+    int n_mblocks;                // user units per user (16 rows each)
     int n_user, n_cand;           // work units in this launch
     int wait_flags;               // users publish and candidates wait (users in the same launch)
     uint32_t spin_limit;

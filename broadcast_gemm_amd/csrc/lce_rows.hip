@@ -5,15 +5,16 @@
 // wave may hold 512 registers) stages the projections it needs in LDS once, then
 // every wave works through a static list of units:
 //
-//   user units      t in [0, n_user): (u, mc) = rows [mc*16*MB, +16*MB) of
+//   user units      t in [0, n_user): (u, blk) = rows [16*blk, +16) of
 //                   P_u[u] = W_u . U[u] in fp32 (IKBO recsys blog, "Deep Dive:
 //                   Linear Compression", stage 1: the user product at its own
-//                   batch size);
+//                   batch size); one row block each, so that the few user
+//                   products are spread over more waves and finish early;
 //   candidate units c in [0, n_cand): (b, mc) = rows of W_c . C[b]; the epilogue
 //                   stores fp32 (unfused ladder stages), stores bf16 (baseline),
 //                   or adds the rows of P_u[map[b]] gathered by index in
-//                   registers and stores Y once (stage 3), waiting for flag
-//                   (map[b], mc) when the user units run in the same launch
+//                   registers and stores Y once (stage 3), waiting for the flags
+//                   of its row blocks of map[b] when the user units run in the same launch
 //                   (stage 4: one launch, user and candidate work overlapped).
 //
 // A wave streams the K steps of consecutive units through one register ring, so
@@ -155,13 +156,14 @@ struct Rows {
             for (int t = 0; t < NT; ++t) v[r][t] = T.acc[mb][t][r];
     }
 
-    // Accumulators = the tile's rows of an fp32 [M][D] matrix.
+    // Accumulators (first MBX row blocks) = the tile's rows of an fp32 [M][D] matrix.
+    template <int MBX = MB>
     static __device__ __forceinline__ void init_from(const RowArgs &a, Tile &T, const float *base, int mrow0, int g,
                                                      int j) {
         const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(base, a.M * D * 4);
         const int o1 = off1(mrow0, g, j, 4), o2 = off2(mrow0, g, j, 4);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+        for (int mb = 0; mb < MBX; ++mb) {
             float v[4][NT];
             load_block(rs, o1, o2, mb, v);
 #pragma unroll
@@ -171,14 +173,14 @@ struct Rows {
         }
     }
 
-    // Tile into an fp32 [M][D] matrix.
-    template <int AUX>
+    // The first MBX row blocks of the tile into an fp32 [M][D] matrix.
+    template <int AUX, int MBX = MB>
     static __device__ __forceinline__ void store_f32(const RowArgs &a, const Tile &T, float *base, int mrow0, int g,
                                                      int j) {
         const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(base, a.M * D * 4);
         const int o1 = off1(mrow0, g, j, 4), o2 = off2(mrow0, g, j, 4);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+        for (int mb = 0; mb < MBX; ++mb) {
             float v[4][NT];
             tile_block(T, mb, v);
             store_block_f32<AUX>(rs, o1, o2, mb, v);
@@ -186,32 +188,34 @@ struct Rows {
     }
 
     // Tile (+ an fp32 [M][D] matrix P when ADD) into a bf16 [M][D] matrix, block by
-    // block: a block's P loads are all in flight together, then its stores follow.
-    template <bool ADD>
+    // block.  With ADD, the next block's P loads are issued before the current block
+    // is added and stored, so two blocks of loads are in flight at a time.
+    template <bool ADD, int MBX = MB>
     static __device__ __forceinline__ void store_bf16(const RowArgs &a, const Tile &T, uint16_t *base,
                                                       const float *pbase, int mrow0, int g, int j) {
         const __amdgpu_buffer_rsrc_t ry = uniform_rsrc(base, a.M * D * 2);
         const int y1 = off1(mrow0, g, j, 2), y2 = off2(mrow0, g, j, 2);
-        __amdgpu_buffer_rsrc_t rp;
-        int p1 = 0, p2 = 0;
         if constexpr (ADD) {
-            rp = uniform_rsrc(pbase, a.M * D * 4);
-            p1 = off1(mrow0, g, j, 4);
-            p2 = off2(mrow0, g, j, 4);
-        }
+            const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(pbase, a.M * D * 4);
+            const int p1 = off1(mrow0, g, j, 4), p2 = off2(mrow0, g, j, 4);
+            float v[2][4][NT];
+            load_block(rp, p1, p2, 0, v[0]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            float v[4][NT];
-            if constexpr (ADD) {
-                load_block(rp, p1, p2, mb, v);
+            for (int mb = 0; mb < MBX; ++mb) {
+                if (mb + 1 < MBX) load_block(rp, p1, p2, mb + 1, v[(mb + 1) & 1]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int t = 0; t < NT; ++t) v[r][t] += T.acc[mb][t][r];
-            } else {
-                tile_block(T, mb, v);
+                    for (int t = 0; t < NT; ++t) v[mb & 1][r][t] += T.acc[mb][t][r];
+                store_block_bf16(ry, y1, y2, mb, v[mb & 1]);
             }
-            store_block_bf16(ry, y1, y2, mb, v);
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < MBX; ++mb) {
+                float v[4][NT];
+                tile_block(T, mb, v);
+                store_block_bf16(ry, y1, y2, mb, v);
+            }
         }
     }
 };
@@ -256,17 +260,29 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     const int nuw = both ? imin_t(a.n_user, n_waves) : 0;   // waves whose first unit is a user unit
     const int V = n_waves - nuw;
     const int wr = n_waves - 1 - w;
-    auto cand_of = [&](int k) {   // k-th candidate unit of this wave (n_cand when none)
+    // Rounds that are complete hold N_full units; the L < T units of a partial last round are
+    // split into their MB row blocks (sub-units of 16 rows), spread over the waves in reverse
+    // order, so that the launch's tail is a third of a unit (MB = 3) rather than a whole one.
+    const int r_full = a.n_cand >= V ? 1 + (a.n_cand - V) / n_waves : 0;
+    const int N_full = r_full > 0 ? V + (r_full - 1) * n_waves : 0;
+    const int n_sub = (a.n_cand - N_full) * MB;
+    auto cand_of = [&](int k) {   // k-th full candidate unit of this wave (N_full when none)
         const int c = w >= nuw ? (k == 0 ? wr : V + (k - 1) * n_waves + wr) : V + k * n_waves + wr;
-        return c < a.n_cand ? c : a.n_cand;
+        return c < N_full ? c : N_full;
     };
+    const int n_mb = a.n_mblocks;   // user units are (u, row block of 16)
     auto user_rsrc = [&](int t) {
-        return t < a.n_user ? uniform_rsrc(a.U + (size_t)(t / n_mc) * a.K_u * D, a.K_u * D * 2)
+        return t < a.n_user ? uniform_rsrc(a.U + (size_t)(t / n_mb) * a.K_u * D, a.K_u * D * 2)
                             : uniform_rsrc(nullptr, 0);
     };
-    auto cand_rsrc = [&](int c) {
-        return c < a.n_cand ? uniform_rsrc(a.C + (size_t)(c / n_mc) * a.K_c * D, a.K_c * D * 2)
+    // X of sub-unit s (none past the last).
+    auto sub_rsrc = [&](int sidx) {
+        return sidx < n_sub ? uniform_rsrc(a.C + (size_t)((N_full + sidx / MB) / n_mc) * a.K_c * D, a.K_c * D * 2)
                             : uniform_rsrc(nullptr, 0);
+    };
+    // X of full unit c; past the full units, the X of this wave's first sub-unit.
+    auto cand_rsrc = [&](int c) {
+        return c < N_full ? uniform_rsrc(a.C + (size_t)(c / n_mc) * a.K_c * D, a.K_c * D * 2) : sub_rsrc(wr);
     };
 
     Tile T;
@@ -300,18 +316,18 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         t = (int)__builtin_amdgcn_readfirstlane(t);
         const int tn = t + n_waves;
         const __amdgpu_buffer_rsrc_t rs_next = tn < a.n_user ? user_rsrc(tn) : cand_rsrc(c);
-        const int mc = t % n_mc;
-        const int u = t / n_mc;
-        const int mrow0 = mc * MB * 16;
+        const int blk = t % n_mb;
+        const int u = t / n_mb;
+        const int mrow0 = blk * 16;
         T.zero();
-        T.run(rs, rs_next, a.n_ks_u, wl_u, a.K_u, a.M, mrow0, g, j);
+        T.template run<1>(rs, rs_next, a.n_ks_u, wl_u, a.K_u, a.M, mrow0, g, j);
         if (!(a.debug_flags & 4u)) {                        // IKBO_FLAG_DEBUG_SKIP_USER: never publish
-            R::template store_f32<kSc1>(a, T, a.P_u + (size_t)u * a.M * D, mrow0, g, j);
+            R::template store_f32<kSc1, 1>(a, T, a.P_u + (size_t)u * a.M * D, mrow0, g, j);
             if (a.wait_flags) {
                 if (a.debug_flags & 2u)                     // IKBO_FLAG_DEBUG_DELAY_USER
                     for (int i = 0; i < 64; ++i) __builtin_amdgcn_s_sleep(127);
                 wait_stores();
-                if (lane == 0) st_flag(&a.flags[2 + u * n_mc + mc], a.epoch);
+                if (lane == 0) st_flag(&a.flags[2 + u * n_mb + blk], a.epoch);
             }
         }
         t = tn;
@@ -324,41 +340,64 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     }
 
     // ---- candidate units (b, mc) ----
+    // The user rows a candidate chunk needs are published per row block.
+    // All of a chunk's flags are read together each poll, so a poll costs one round trip.
+    auto wait_user = [&](int u, int mc, int blk0 = 0, int nblk = MB) {
+        const uint32_t *f = &a.flags[2 + u * n_mb + mc * MB + blk0];
+        const int nb = imin_t(nblk, n_mb - mc * MB - blk0);
+        uint32_t polls = 0;
+        for (;;) {
+            uint32_t v[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) v[i] = i < nb ? ld_flag(f + i) : a.epoch;
+            bool ok = true;
+#pragma unroll
+            for (int i = 0; i < MB; ++i) ok = ok && __builtin_amdgcn_readfirstlane(v[i]) == a.epoch;
+            if (ok) break;
+            if (++polls >= a.spin_limit) {
+                if (lane == 0) atomicOr(a.err, ERRBIT_TIMEOUT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");   // P_u loads stay after the flags
+    };
     // Gather-add epilogue after waiting for the user flag (bounded): Y = tile + P_u[map[b]].
-    auto add_user_store = [&](const Tile &X, int cc) {
+    auto add_user_store = [&](const Tile &X, int cc, int u) {
         const int mc = cc % n_mc;
         const int b = cc / n_mc;
-        const int u = (int)__builtin_amdgcn_readfirstlane(a.map[b]);
         if (u < 0 || u >= a.B_u) {
             if (lane == 0) atomicOr(a.err, ERRBIT_MAP);
             return;
         }
-        if (a.wait_flags) wait_flag(a, &a.flags[2 + u * n_mc + mc], lane);
+        if (a.wait_flags) wait_user(u, mc);
         R::template store_bf16<true>(a, X, static_cast<uint16_t *>(a.out) + (size_t)b * a.M * D,
                                      a.P_u + (size_t)u * a.M * D, mc * MB * 16, g, j);
     };
     if constexpr (EPI == EPI_ADD_USER) {
-        if (a.wait_flags && c < a.n_cand) {
+        if (a.wait_flags && c < N_full) {
             // With the users in the same launch, a wave's first two candidate units run their K
             // loops back to back (two sets of accumulators) before either epilogue, so the first
             // wait for a user product comes after two units' worth of reads.
             const int c1 = cand_of(1), c2 = cand_of(2);
             const __amdgpu_buffer_rsrc_t rs1 = cand_rsrc(c1), rs2 = cand_rsrc(c2);
+            const int u0 = (int)__builtin_amdgcn_readfirstlane(a.map[c / n_mc]);
+            const int u1 = c1 < N_full ? (int)__builtin_amdgcn_readfirstlane(a.map[c1 / n_mc]) : 0;
             T.zero();
             T.run(rs, rs1, a.n_ks_c, wl_c, a.K_wc, a.M, (c % n_mc) * MB * 16, g, j);
             const Tile T0 = T;
-            if (c1 < a.n_cand) {
+            if (c1 < N_full) {
                 T.zero();
                 T.run(rs1, rs2, a.n_ks_c, wl_c, a.K_wc, a.M, (c1 % n_mc) * MB * 16, g, j);
             }
-            add_user_store(T0, c);
-            if (c1 < a.n_cand) add_user_store(T, c1);
+            add_user_store(T0, c, u0);
+            if (c1 < N_full) add_user_store(T, c1, u1);
             c = c2;
             kc = 2;
             rs = rs2;
         }
     }
-    while (c < a.n_cand) {
+    while (c < N_full) {
         c = (int)__builtin_amdgcn_readfirstlane(c);
         const int cn = cand_of(kc + 1);
         const __amdgpu_buffer_rsrc_t rs_next = cand_rsrc(cn);
@@ -373,7 +412,7 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
             const int u = (int)__builtin_amdgcn_readfirstlane(a.map[b]);
             const bool valid = u >= 0 && u < a.B_u;
             if (valid) {
-                if (a.wait_flags) wait_flag(a, &a.flags[2 + u * n_mc + mc], lane);
+                if (a.wait_flags) wait_user(u, mc);
                 R::init_from(a, T, a.P_u + (size_t)u * a.M * D, mrow0, g, j);
             }
             T.run(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
@@ -390,6 +429,43 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         }
         c = cn;
         ++kc;
+        rs = rs_next;
+    }
+
+    // ---- candidate sub-units (b, mc, one row block) of the partial last round ----
+    for (int sidx = wr; sidx < n_sub;) {
+        sidx = (int)__builtin_amdgcn_readfirstlane(sidx);
+        const int sn = sidx + n_waves;
+        const __amdgpu_buffer_rsrc_t rs_next = sub_rsrc(sn);
+        const int unit = N_full + sidx / MB;
+        const int blk = sidx % MB;
+        const int mc = unit % n_mc;
+        const int b = unit / n_mc;
+        const int mrow0 = mc * MB * 16 + blk * 16;
+        const size_t obase = (size_t)b * a.M * D;
+        T.zero();
+        if constexpr (EPI == EPI_ADD_USER) {
+            const int u = (int)__builtin_amdgcn_readfirstlane(a.map[b]);
+            const bool valid = u >= 0 && u < a.B_u;
+            if (valid) {
+                if (a.wait_flags) wait_user(u, mc, blk, 1);
+                R::template init_from<1>(a, T, a.P_u + (size_t)u * a.M * D, mrow0, g, j);
+            }
+            T.template run<1>(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
+            if (valid)
+                R::template store_bf16<false, 1>(a, T, static_cast<uint16_t *>(a.out) + obase, nullptr, mrow0, g,
+                                                 j);
+            else if (lane == 0)
+                atomicOr(a.err, ERRBIT_MAP);
+        } else {
+            T.template run<1>(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
+            if constexpr (EPI == EPI_STORE_F32)
+                R::template store_f32<0, 1>(a, T, static_cast<float *>(a.out) + obase, mrow0, g, j);
+            else
+                R::template store_bf16<false, 1>(a, T, static_cast<uint16_t *>(a.out) + obase, nullptr, mrow0, g,
+                                                 j);
+        }
+        sidx = sn;
         rs = rs_next;
     }
 }

@@ -123,19 +123,19 @@ struct RowTile {
         }
     }
 
-    // Multiply the step in ring slot S (K step ks) into the accumulators.  W is an
-    // M x K matrix in LDS (rows K elements long); the tile's rows start at mrow0.
-    // On the last step (tail) elements at or past K are masked, and rows at or past
-    // M read as zero (ragged).
-    template <int S>
+    // Multiply the step in ring slot S (K step ks) into the first MBX row blocks of
+    // the accumulators.  W is an M x K matrix in LDS (rows K elements long); the
+    // tile's rows start at mrow0.  On the last step (tail) elements at or past K are
+    // masked, and rows at or past M read as zero (ragged).
+    template <int S, int MBX>
     __device__ __forceinline__ void compute(const uint16_t *wl, int K, int M, int mrow0, int ks, bool tail,
                                             bool ragged, int g, int j) {
         u32x4_t b1[N8 ? 8 : 1], b2[W2 ? W2 : 1];
         if constexpr (N8 != 0) transpose_rows<8>(r1[S], b1);
         if constexpr (W2 != 0) transpose_rows<W2>(r2[S], b2);
-        u32x4_t av[MB];
+        u32x4_t av[MBX];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+        for (int mb = 0; mb < MBX; ++mb) {
             const int m = mrow0 + 16 * mb + j;
             const int mr = m < M ? m : M - 1;
             __builtin_memcpy(&av[mb], wl + mr * K + ks * 32 + 8 * g, 16);
@@ -146,16 +146,16 @@ struct RowTile {
             for (int w = 0; w < 4; ++w) {
                 const uint32_t keep = lim >= 2 * w + 2 ? 0xFFFFFFFFu : (lim == 2 * w + 1 ? 0xFFFFu : 0u);
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) av[mb][w] &= keep;
+                for (int mb = 0; mb < MBX; ++mb) av[mb][w] &= keep;
             }
         }
         if (ragged) {
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < MBX; ++mb)
                 if (mrow0 + 16 * mb + j >= M) av[mb] = (u32x4_t){0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+        for (int mb = 0; mb < MBX; ++mb) {
             if constexpr (N8 != 0) {
 #pragma unroll
                 for (int t = 0; t < 8; ++t) acc[mb][t] = mfma_bf16(av[mb], b1[t], acc[mb][t]);
@@ -177,25 +177,28 @@ struct RowTile {
     // fall past the padded end go to the first NS-1 steps of the next matrix
     // (rs_next; a zero-sized resource when there is none), so the ring holds the
     // next unit's opening steps while this unit's epilogue runs.
-    template <int S>
+    template <int S, int MBX>
     __device__ __forceinline__ void step(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rs_next, int ks,
                                          int n_ks, int nsp, const uint16_t *wl, int K, int M, int mrow0,
                                          bool ragged, int g, int j) {
         const int kk = ks + S + NS - 1;
         const bool cur = kk < nsp;
         load<(S + NS - 1) % NS>(cur ? rs : rs_next, cur ? kk : kk - nsp);
-        if (ks + S < n_ks) compute<S>(wl, K, M, mrow0, ks + S, ks + S == n_ks - 1, ragged, g, j);
+        if (ks + S < n_ks) compute<S, MBX>(wl, K, M, mrow0, ks + S, ks + S == n_ks - 1, ragged, g, j);
     }
 
+    // MBX <= MB row blocks from mrow0 (accumulator blocks 0 .. MBX-1).
+    template <int MBX = MB>
     __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rs_next, int n_ks,
                                         const uint16_t *wl, int K, int M, int mrow0, int g, int j) {
+        static_assert(MBX >= 1 && MBX <= MB, "row blocks");
         const int nsp = (n_ks + NS - 1) / NS * NS;
-        const bool ragged = mrow0 + 16 * MB > M;
+        const bool ragged = mrow0 + 16 * MBX > M;
         for (int ks = 0; ks < nsp; ks += NS) {
-            step<0>(rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
-            if constexpr (NS > 1) step<1>(rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
-            if constexpr (NS > 2) step<2>(rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
-            if constexpr (NS > 3) step<3>(rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
+            step<0, MBX>(rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
+            if constexpr (NS > 1) step<1, MBX>(rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
+            if constexpr (NS > 2) step<2, MBX>(rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
+            if constexpr (NS > 3) step<3, MBX>(rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
         }
     }
 
