@@ -257,7 +257,9 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     // on waves that did no user work.
     const int w = first;
     const bool both = a.n_user > 0 && a.n_cand > 0;
-    const int nuw = both ? imin_t(a.n_user, n_waves) : 0;   // waves whose first unit is a user unit
+    // Waves of the blocks that hold user units (whole blocks: those blocks stage W_c only
+    // after their users, so none of their waves should hold a round-0 candidate unit).
+    const int nuw = both ? imin_t((a.n_user + wpb - 1) / wpb * wpb, n_waves) : 0;
     const int V = n_waves - nuw;
     const int wr = n_waves - 1 - w;
     // Rounds that are complete hold N_full units; the L < T units of a partial last round are
