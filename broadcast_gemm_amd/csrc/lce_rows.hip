@@ -54,6 +54,16 @@ __device__ __forceinline__ void st_flag(uint32_t *p, uint32_t v) {
 constexpr int kSc1 = 16;   // buffer cache-policy bit sc1: device scope (write through this XCD's L2)
 constexpr int kNt = 2;     // buffer cache-policy bit nt: non-temporal (streaming) stores
 
+// A copy of x in a vector register.  Store data is routed through this: the
+// compiler otherwise stores accumulators straight from AGPRs and then reuses
+// those AGPRs for the next store's data a cycle or two later, before the wide
+// store has read all of them (seen on gfx950 as corrupted rows of fp32 tiles).
+__device__ __forceinline__ float in_vgpr(float x) {
+    float y;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+    return y;
+}
+
 // Wait until every store this wave issued has been acknowledged.  Stores made
 // with kSc1 are then visible to every XCD, and a flag or counter update issued
 // afterwards publishes them.  The asm also keeps the compiler from moving
@@ -153,7 +163,7 @@ struct Rows {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) v[r][t] = T.acc[mb][t][r];
+            for (int t = 0; t < NT; ++t) v[r][t] = in_vgpr(T.acc[mb][t][r]);
     }
 
     // Accumulators (first MBX row blocks) = the tile's rows of an fp32 [M][D] matrix.

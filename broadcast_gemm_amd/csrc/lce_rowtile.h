@@ -128,8 +128,8 @@ struct RowTile {
     // tile's rows start at mrow0.  On the last step (tail) elements at or past K are
     // masked, and rows at or past M read as zero (ragged).
     template <int S, int MBX>
-    __device__ __forceinline__ void compute(const uint16_t *wl, int K, int M, int mrow0, int ks, bool tail,
-                                            bool ragged, int g, int j) {
+    __device__ __forceinline__ void compute(f32x4_t (&A)[MB][NT], const uint16_t *wl, int K, int M, int mrow0, int ks,
+                                            bool tail, bool ragged, int g, int j) {
         u32x4_t b1[N8 ? 8 : 1], b2[W2 ? W2 : 1];
         if constexpr (N8 != 0) transpose_rows<8>(r1[S], b1);
         if constexpr (W2 != 0) transpose_rows<W2>(r2[S], b2);
@@ -158,10 +158,10 @@ struct RowTile {
         for (int mb = 0; mb < MBX; ++mb) {
             if constexpr (N8 != 0) {
 #pragma unroll
-                for (int t = 0; t < 8; ++t) acc[mb][t] = mfma_bf16(av[mb], b1[t], acc[mb][t]);
+                for (int t = 0; t < 8; ++t) A[mb][t] = mfma_bf16(av[mb], b1[t], A[mb][t]);
             }
 #pragma unroll
-            for (int t = 0; t < W2; ++t) acc[mb][NT1 + t] = mfma_bf16(av[mb], b2[t], acc[mb][NT1 + t]);
+            for (int t = 0; t < W2; ++t) A[mb][NT1 + t] = mfma_bf16(av[mb], b2[t], A[mb][NT1 + t]);
         }
     }
 
@@ -178,28 +178,36 @@ struct RowTile {
     // (rs_next; a zero-sized resource when there is none), so the ring holds the
     // next unit's opening steps while this unit's epilogue runs.
     template <int S, int MBX>
-    __device__ __forceinline__ void step(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rs_next, int ks,
-                                         int n_ks, int nsp, const uint16_t *wl, int K, int M, int mrow0,
-                                         bool ragged, int g, int j) {
+    __device__ __forceinline__ void step(f32x4_t (&A)[MB][NT], __amdgpu_buffer_rsrc_t rs,
+                                         __amdgpu_buffer_rsrc_t rs_next, int ks, int n_ks, int nsp,
+                                         const uint16_t *wl, int K, int M, int mrow0, bool ragged, int g, int j) {
         const int kk = ks + S + NS - 1;
         const bool cur = kk < nsp;
         load<(S + NS - 1) % NS>(cur ? rs : rs_next, cur ? kk : kk - nsp);
-        if (ks + S < n_ks) compute<S, MBX>(wl, K, M, mrow0, ks + S, ks + S == n_ks - 1, ragged, g, j);
+        if (ks + S < n_ks) compute<S, MBX>(A, wl, K, M, mrow0, ks + S, ks + S == n_ks - 1, ragged, g, j);
     }
 
-    // MBX <= MB row blocks from mrow0 (accumulator blocks 0 .. MBX-1).
+    // MBX <= MB row blocks from mrow0, accumulated into blocks 0 .. MBX-1 of A (a tile's
+    // own accumulators, or another tile's: the ring belongs to this tile either way).
     template <int MBX = MB>
-    __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rs_next, int n_ks,
-                                        const uint16_t *wl, int K, int M, int mrow0, int g, int j) {
+    __device__ __forceinline__ void run_into(f32x4_t (&A)[MB][NT], __amdgpu_buffer_rsrc_t rs,
+                                             __amdgpu_buffer_rsrc_t rs_next, int n_ks, const uint16_t *wl, int K,
+                                             int M, int mrow0, int g, int j) {
         static_assert(MBX >= 1 && MBX <= MB, "row blocks");
         const int nsp = (n_ks + NS - 1) / NS * NS;
         const bool ragged = mrow0 + 16 * MBX > M;
         for (int ks = 0; ks < nsp; ks += NS) {
-            step<0, MBX>(rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
-            if constexpr (NS > 1) step<1, MBX>(rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
-            if constexpr (NS > 2) step<2, MBX>(rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
-            if constexpr (NS > 3) step<3, MBX>(rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
+            step<0, MBX>(A, rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
+            if constexpr (NS > 1) step<1, MBX>(A, rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
+            if constexpr (NS > 2) step<2, MBX>(A, rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
+            if constexpr (NS > 3) step<3, MBX>(A, rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
         }
+    }
+
+    template <int MBX = MB>
+    __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rs_next, int n_ks,
+                                        const uint16_t *wl, int K, int M, int mrow0, int g, int j) {
+        run_into<MBX>(acc, rs, rs_next, n_ks, wl, K, M, mrow0, g, j);
     }
 
     // Column of output t for lane slot j.
