@@ -305,22 +305,25 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     __amdgpu_buffer_rsrc_t rs = t < a.n_user ? user_rsrc(t) : cand_rsrc(c);
 
     // ---- stage the projections.  LDS: [W_c if candidates run][W_u if users run], each
-    // lds_w_elems(M, K) elements, copied as is.  The first unit's opening steps go out
-    // right behind the first projection loads, so their memory latency overlaps the
-    // staging.  Blocks that hold user units of a launch with both kinds stage W_u first
-    // and W_c only after their user units, so that the user products (which candidates
-    // wait for) start early.
+    // lds_w_elems(M, K) elements, copied as is.  The first unit's first step goes out
+    // ahead of the projection loads and its other opening steps right behind them, so
+    // their memory latency overlaps the staging.  Blocks that hold user units of a
+    // launch with both kinds stage W_u first and W_c only after their user units, so
+    // that the user products (which candidates wait for) start early.
     extern __shared__ __align__(16) uint16_t lds[];
     uint16_t *wl_c = lds;
     uint16_t *wl_u = lds + (a.n_cand > 0 ? lds_w_elems(a.M, a.K_wc) : 0);
     const bool need_u = (int)blockIdx.x * wpb < a.n_user;   // this block holds user units
-    auto prologue = [&]() { T.prologue(rs); };
+    // Batches: 15 blocks of 16 bytes per thread cover W_u of 96 x 301 and 10 cover W_c of
+    // 96 x 197; with the opening steps that makes at most 63 loads per wave in flight.
+    T.prologue_first(rs);
+    auto rest = [&]() { T.prologue_rest(rs); };
     if (need_u)
-        stage_flat(a.W_u, a.M * a.K_u, wl_u, prologue);
+        stage_flat<15>(a.W_u, a.M * a.K_u, wl_u, rest);
     else if (a.n_cand > 0)
-        stage_flat(a.W_c, a.M * a.K_wc, wl_c, prologue);
+        stage_flat<10>(a.W_c, a.M * a.K_wc, wl_c, rest);
     else
-        prologue();
+        rest();
     __syncthreads();
 
     // ---- user units ----
@@ -347,7 +350,7 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     }
     if (need_u && both) {
         // The ring already holds the first candidate unit's opening steps.
-        stage_flat(a.W_c, a.M * a.K_wc, wl_c, [] {});
+        stage_flat<10>(a.W_c, a.M * a.K_wc, wl_c, [] {});
         __syncthreads();
     }
 
@@ -484,14 +487,18 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
 
 typedef void (*rows_kernel_t)(RowArgs);
 
+// Row blocks per unit that a layout may use (at most 128 accumulators per lane, as
+// rows_max_mb computes); only those are instantiated.
+constexpr int layout_max_mb(int N8, int W2) { return 32 / (8 * N8 + W2) > 4 ? 4 : 32 / (8 * N8 + W2); }
+
 template <int N8, int W2, int EPI>
 rows_kernel_t pick_mb(int mb) {
-    switch (mb) {
-        case 1: return lce_rows_kernel<1, N8, W2, EPI>;
-        case 2: return lce_rows_kernel<2, N8, W2, EPI>;
-        case 3: return lce_rows_kernel<3, N8, W2, EPI>;
-        case 4: return lce_rows_kernel<4, N8, W2, EPI>;
-    }
+    constexpr int mx = layout_max_mb(N8, W2);
+    if (mb < 1 || mb > mx) return nullptr;
+    if (mb == 1) return lce_rows_kernel<1, N8, W2, EPI>;
+    if constexpr (mx >= 2) if (mb == 2) return lce_rows_kernel<2, N8, W2, EPI>;
+    if constexpr (mx >= 3) if (mb == 3) return lce_rows_kernel<3, N8, W2, EPI>;
+    if constexpr (mx >= 4) if (mb == 4) return lce_rows_kernel<4, N8, W2, EPI>;
     return nullptr;
 }
 

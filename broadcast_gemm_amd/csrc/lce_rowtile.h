@@ -50,14 +50,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *p, in
 // ---- staging of the projections into LDS ----------------------------------------------
 
 // Copy n elements of a projection (16-byte aligned base) into LDS at F with
-// coalesced 16-byte loads and writes.  The buffer range covers the matrix
-// rounded up to 16 bytes (its last 16-byte block, which holds its last
-// element).  All loads of a thread are issued before any is written; `issued`
-// runs right after the first batch so that the caller can put other memory
-// traffic in flight behind it.  The caller synchronises before F is read.
-template <typename Issued>
+// coalesced 16-byte loads and writes, CB blocks per thread per batch.  The
+// buffer range covers the matrix rounded up to 16 bytes (its last 16-byte
+// block, which holds its last element).  All loads of a batch are issued before
+// any is written; `issued` runs right after the first batch so that the caller
+// can put other memory traffic in flight behind it.  The caller sizes CB so
+// that one batch covers the matrix and, with what it issues around it, a wave
+// stays within the 63 vector-memory operations it can have outstanding (past
+// that, issue stalls until the oldest completes).  The caller synchronises
+// before F is read.
+template <int CB, typename Issued>
 __device__ __forceinline__ void stage_flat(const uint16_t *W, int n, uint16_t *F, Issued &&issued) {
-    constexpr int CB = 16;   // 16-byte blocks per thread in flight
     const int nt = (int)blockDim.x;
     const int tid = (int)threadIdx.x;
     const int nblk = (n + 7) / 8;
@@ -167,7 +170,15 @@ struct RowTile {
 
     // Issue the first NS-1 steps of a matrix (ring slots 0 .. NS-2).
     __device__ __forceinline__ void prologue(__amdgpu_buffer_rsrc_t rs) {
+        prologue_first(rs);
+        prologue_rest(rs);
+    }
+    // The same in two parts: step 0 alone (so that it can go out ahead of other
+    // traffic), then steps 1 .. NS-2.
+    __device__ __forceinline__ void prologue_first(__amdgpu_buffer_rsrc_t rs) {
         if constexpr (NS > 1) load<0>(rs, 0);
+    }
+    __device__ __forceinline__ void prologue_rest(__amdgpu_buffer_rsrc_t rs) {
         if constexpr (NS > 2) load<1>(rs, 1);
         if constexpr (NS > 3) load<2>(rs, 2);
     }
