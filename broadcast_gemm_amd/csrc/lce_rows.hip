@@ -267,9 +267,8 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     // on waves that did no user work.
     const int w = first;
     const bool both = a.n_user > 0 && a.n_cand > 0;
-    // Waves of the blocks that hold user units (whole blocks: those blocks stage W_c only
-    // after their users, so none of their waves should hold a round-0 candidate unit).
-    const int nuw = both ? imin_t((a.n_user + wpb - 1) / wpb * wpb, n_waves) : 0;
+    // Waves that hold a user unit (the first n_user; n_user <= T in a launch with both).
+    const int nuw = both ? imin_t(a.n_user, n_waves) : 0;
     const int V = n_waves - nuw;
     const int wr = n_waves - 1 - w;
     // Rounds that are complete hold N_full units; the L < T units of a partial last round are
@@ -307,9 +306,8 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     // ---- stage the projections.  LDS: [W_c if candidates run][W_u if users run], each
     // lds_w_elems(M, K) elements, copied as is.  The first unit's first step goes out
     // ahead of the projection loads and its other opening steps right behind them, so
-    // their memory latency overlaps the staging.  Blocks that hold user units of a
-    // launch with both kinds stage W_u first and W_c only after their user units, so
-    // that the user products (which candidates wait for) start early.
+    // their memory latency overlaps the staging.  Blocks that hold user units stage W_u
+    // first (the user products, which candidates wait for, start with it), then W_c.
     extern __shared__ __align__(16) uint16_t lds[];
     uint16_t *wl_c = lds;
     uint16_t *wl_u = lds + (a.n_cand > 0 ? lds_w_elems(a.M, a.K_wc) : 0);
@@ -318,8 +316,10 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     // 96 x 197; with the opening steps that makes at most 63 loads per wave in flight.
     T.prologue_first(rs);
     auto rest = [&]() { T.prologue_rest(rs); };
-    if (need_u)
+    if (need_u) {
         stage_flat<15>(a.W_u, a.M * a.K_u, wl_u, rest);
+        if (a.n_cand > 0) stage_flat<10>(a.W_c, a.M * a.K_wc, wl_c, [] {});
+    }
     else if (a.n_cand > 0)
         stage_flat<10>(a.W_c, a.M * a.K_wc, wl_c, rest);
     else
@@ -347,11 +347,6 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         }
         t = tn;
         rs = rs_next;
-    }
-    if (need_u && both) {
-        // The ring already holds the first candidate unit's opening steps.
-        stage_flat<10>(a.W_c, a.M * a.K_wc, wl_c, [] {});
-        __syncthreads();
     }
 
     // ---- candidate units (b, mc) ----
