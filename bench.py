@@ -114,15 +114,38 @@ def _mean_kib(d: str, counter: str, match: str) -> tuple:
     return sum(vals) / len(vals), len(vals)
 
 
+def _forward_kib(d: str, counter: str) -> tuple:
+    """Per-forward sum over the launches of a forward: the mean of each distinct (kernel, grid)
+    that is not a runtime copy or fill (each appears once per forward in every ladder stage)."""
+    groups = {}
+    for r in _counter_rows(d, counter):
+        name = r.get("Kernel_Name", "")
+        if "__amd_rocclr" in name:
+            continue
+        groups.setdefault((name, r.get("Grid_Size")), []).append(float(r["Counter_Value"]))
+    if not groups:
+        raise SystemExit(f"no {counter} rows under {d}")
+    total = sum(sum(v) / len(v) for v in groups.values())
+    return total, {f"{k[0]} grid={k[1]}": [round(sum(v) / len(v), 1), len(v)] for k, v in groups.items()}
+
+
 def run_traffic(args) -> int:
     """Write profiles/traffic_<workload>_<variant>.json from four rocprofv3 --pmc runs (no GPU).
 
-    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the forward kernel are scaled by what
-    the same counters read for a plain device copy of known size."""
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the forward kernel (or, with
+    --all-kernels, summed over the launches of one forward) are scaled by what the same
+    counters read for a plain device copy of known size."""
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic
     copy_bytes = args.copy_mib << 20
-    f_kib, nf = _mean_kib(fetch_dir, "FETCH_SIZE", args.kernel_match)
-    w_kib, nw = _mean_kib(write_dir, "WRITE_SIZE", args.kernel_match)
+    kernels = None
+    if args.all_kernels:
+        f_kib, fk = _forward_kib(fetch_dir, "FETCH_SIZE")
+        w_kib, wk = _forward_kib(write_dir, "WRITE_SIZE")
+        nf, nw = len(fk), len(wk)
+        kernels = {"FETCH_SIZE": fk, "WRITE_SIZE": wk}
+    else:
+        f_kib, nf = _mean_kib(fetch_dir, "FETCH_SIZE", args.kernel_match)
+        w_kib, nw = _mean_kib(write_dir, "WRITE_SIZE", args.kernel_match)
     cf_kib, _ = _mean_kib(cfetch_dir, "FETCH_SIZE", args.copy_match)
     cw_kib, _ = _mean_kib(cwrite_dir, "WRITE_SIZE", args.copy_match)
     kf = copy_bytes / (cf_kib * 1024.0)
@@ -131,7 +154,8 @@ def run_traffic(args) -> int:
     write_b = w_kib * 1024.0 * kw
     from broadcast_gemm_amd.inputs import CONFIG_BY_NAME
     cfg = CONFIG_BY_NAME[args.config]
-    out = {"workload": cfg.name, "variant": args.variant, "kernel_match": args.kernel_match,
+    out = {"workload": cfg.name, "variant": args.variant,
+           "kernel_match": "all launches of a forward" if args.all_kernels else args.kernel_match,
            "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
            "dispatches": [nf, nw], "copy_bytes": copy_bytes,
            "copy_fetch_kib": round(cf_kib, 1), "copy_write_kib": round(cw_kib, 1),
@@ -139,6 +163,8 @@ def run_traffic(args) -> int:
            "hbm_fetch_bytes_per_launch": round(fetch_b), "hbm_write_bytes_per_launch": round(write_b),
            "hbm_bytes_per_launch": round(fetch_b + write_b),
            "algorithmic_bytes": algorithmic_bytes(cfg), "kernel_source_hash": kernel_source_hash()}
+    if kernels is not None:
+        out["per_kernel_kib"] = kernels
     path = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}_{args.variant}.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -175,6 +201,8 @@ def main() -> int:
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="--mode traffic: rocprofv3 --pmc output directories")
     ap.add_argument("--kernel-match", default="lce_rows_kernel")
+    ap.add_argument("--all-kernels", action="store_true",
+                    help="--mode traffic: sum every launch of one forward (multi-launch ladder stages)")
     ap.add_argument("--copy-match", default="copyBuffer")
     args = ap.parse_args()
     if args.mode == "traffic":

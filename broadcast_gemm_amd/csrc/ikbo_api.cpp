@@ -43,6 +43,7 @@ struct ikbo_lce_plan_s {
     int n_ucols_max, fused_grid, fused_bpc;
     // rows engine
     int rows_mb;
+    int rows_lds_shared;            // S4: W_u and W_c share one LDS region (their sum does not fit)
     int bpc_user, bpc_cand, bpc_both;
     // user split-K (fused paths and the rows engine's user launches)
     int ksplit, ks_per_split;
@@ -152,10 +153,12 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
         // The staged projections (as is, plus slack) must fit one workgroup's LDS.
         const size_t lds_u = (size_t)lds_w_elems(M, K_u) * 2, lds_c = (size_t)lds_w_elems(M, K_c) * 2;
         const size_t lds_cat = (size_t)lds_w_elems(M, ceil_div(K_u + K_c, 32) * 32) * 2;
+        // In S4, blocks with user units hold W_u and W_c together when both fit, else one after
+        // the other in the same region.
         bool fits;
         if (variant == IKBO_S0_MATERIALISED) fits = lds_cat <= (size_t)max_lds;
-        else if (variant == IKBO_S4_PERSISTENT) fits = lds_u + lds_c <= (size_t)max_lds;
         else fits = std::max(lds_u, lds_c) <= (size_t)max_lds;
+        p->rows_lds_shared = variant == IKBO_S4_PERSISTENT && lds_u + lds_c > (size_t)max_lds ? 1 : 0;
         // Epilogue byte offsets within one fp32 [M_pad][D] matrix are 32-bit.
         if (fits && (long long)mpad * D * 4 < (1LL << 31)) {
             p->engine = ENGINE_ROWS;
@@ -249,6 +252,7 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
                                                          : EPI_ADD_USER;
         auto bpc = [&](int nu, int nc) {
             r.n_user = nu; r.n_cand = nc;
+            r.lds_shared = nu > 0 && nc > 0 ? p->rows_lds_shared : 0;
             if (rows_lds_bytes(r) > (size_t)max_lds) return 0;
             return rows_blocks_per_cu(epi, D, p->rows_mb, rows_lds_bytes(r));
         };
@@ -413,6 +417,7 @@ int forward_rows(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t 
             if (cap == hipStreamCaptureStatusNone && n_user <= waves) {
                 RowArgs f = a;
                 f.n_user = n_user; f.n_cand = n_cand; f.out = Y; f.wait_flags = 1;
+                f.lds_shared = p->rows_lds_shared;
                 f.epoch = ++p->epoch;
                 if (f.epoch == 0) f.epoch = ++p->epoch;   // 0 is the flags' initial value
                 if ((e = rows_launch(p, EPI_ADD_USER, f, p->bpc_both, s)) != hipSuccess) return hip_fail(e, "fused");

@@ -267,8 +267,11 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     // on waves that did no user work.
     const int w = first;
     const bool both = a.n_user > 0 && a.n_cand > 0;
-    // Waves that hold a user unit (the first n_user; n_user <= T in a launch with both).
-    const int nuw = both ? imin_t(a.n_user, n_waves) : 0;
+    // Waves that hold a user unit (the first n_user; n_user <= T in a launch with both).  When
+    // W_u and W_c take turns in LDS, a block with user units has W_c only after them, so whole
+    // blocks count as user waves and none of their waves holds a round-0 candidate unit.
+    const bool shared = both && a.lds_shared;
+    const int nuw = both ? imin_t(shared ? (a.n_user + wpb - 1) / wpb * wpb : a.n_user, n_waves) : 0;
     const int V = n_waves - nuw;
     const int wr = n_waves - 1 - w;
     // Rounds that are complete hold N_full units; the L < T units of a partial last round are
@@ -310,7 +313,7 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     // first (the user products, which candidates wait for, start with it), then W_c.
     extern __shared__ __align__(16) uint16_t lds[];
     uint16_t *wl_c = lds;
-    uint16_t *wl_u = lds + (a.n_cand > 0 ? lds_w_elems(a.M, a.K_wc) : 0);
+    uint16_t *wl_u = lds + (a.n_cand > 0 && !shared ? lds_w_elems(a.M, a.K_wc) : 0);
     const bool need_u = (int)blockIdx.x * wpb < a.n_user;   // this block holds user units
     // Batches: 15 blocks of 16 bytes per thread cover W_u of 96 x 301 and 10 cover W_c of
     // 96 x 197; with the opening steps that makes at most 63 loads per wave in flight.
@@ -318,7 +321,7 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     auto rest = [&]() { T.prologue_rest(rs); };
     if (need_u) {
         stage_flat<15>(a.W_u, a.M * a.K_u, wl_u, rest);
-        if (a.n_cand > 0) stage_flat<10>(a.W_c, a.M * a.K_wc, wl_c, [] {});
+        if (a.n_cand > 0 && !shared) stage_flat<10>(a.W_c, a.M * a.K_wc, wl_c, [] {});
     }
     else if (a.n_cand > 0)
         stage_flat<10>(a.W_c, a.M * a.K_wc, wl_c, rest);
@@ -347,6 +350,13 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         }
         t = tn;
         rs = rs_next;
+    }
+    if (need_u && shared) {
+        // W_c replaces W_u once every wave of the block is done with it; the ring already
+        // holds the first candidate unit's opening steps.
+        __syncthreads();
+        stage_flat<10>(a.W_c, a.M * a.K_wc, wl_c, [] {});
+        __syncthreads();
     }
 
     // ---- candidate units (b, mc) ----
@@ -530,10 +540,9 @@ int rows_max_mb(int D) {
 }
 
 size_t rows_lds_bytes(const RowArgs &a) {
-    size_t b = 0;
-    if (a.n_cand > 0) b += (size_t)lds_w_elems(a.M, a.K_wc) * 2;
-    if (a.n_user > 0) b += (size_t)lds_w_elems(a.M, a.K_u) * 2;
-    return b;
+    const size_t c = a.n_cand > 0 ? (size_t)lds_w_elems(a.M, a.K_wc) * 2 : 0;
+    const size_t u = a.n_user > 0 ? (size_t)lds_w_elems(a.M, a.K_u) * 2 : 0;
+    return a.lds_shared && a.n_user > 0 && a.n_cand > 0 ? std::max(c, u) : c + u;
 }
 
 int rows_blocks_per_cu(int epi, int D, int mb, size_t lds_bytes) {
