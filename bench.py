@@ -173,6 +173,53 @@ def run_traffic(args) -> int:
     return 0
 
 
+def run_rewrite(args, cfg, sets) -> int:
+    """An unmodified model's materialised broadcast (cat of U[map] and C, then one batched
+    matmul with [W_u | W_c], in torch on the GPU) against the same module after the
+    inference-time rewrite (broadcast_gemm_amd.rewrite), on the rotated input sets."""
+    import torch
+    import torch.fx as fx
+    from broadcast_gemm_amd import rewrite as rw
+
+    class Materialised(torch.nn.Module):
+        def __init__(self, W):
+            super().__init__()
+            self.W = torch.nn.Parameter(W, requires_grad=False)
+
+        def forward(self, U, C, mp):
+            return torch.matmul(self.W, torch.cat([U[mp], C], dim=1))
+
+    U0, C0, mp0, W_u, W_c = sets[0][:5]
+    model = Materialised(torch.cat([W_u, W_c], dim=1).contiguous()).cuda()
+    maps = [s[2].long() for s in sets]
+    gm = fx.symbolic_trace(model)
+    assert rw.rewrite_lce(gm, U0, C0, maps[0]) == 1
+
+    def timed(fn):
+        with torch.no_grad():
+            for i in range(args.warmup):
+                s = sets[i % len(sets)]
+                fn(s[0], s[1], maps[i % len(sets)])
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(args.steps):
+                s = sets[i % len(sets)]
+                fn(s[0], s[1], maps[i % len(sets)])
+            e1.record()
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / args.steps
+
+    t_mat = timed(model)
+    t_rw = timed(gm)
+    st = rw.plan_table().check_all()
+    out = {"mode": "rewrite", "config": cfg.name, "steps": args.steps, "warmup": args.warmup,
+           "materialised_torch_us": round(t_mat, 3), "rewritten_ikbo_us": round(t_rw, 3),
+           "speedup": round(t_mat / t_rw, 2), "device_status": st, "rotating_sets": len(sets)}
+    print(json.dumps(out), flush=True)
+    return 0 if st == 0 else 1
+
+
 def run_copy(args) -> int:
     """Plain device copy of known size (calibrates FETCH_SIZE/WRITE_SIZE counters)."""
     import torch
@@ -196,7 +243,7 @@ def main() -> int:
     ap.add_argument("--rotate-mb", type=int, default=1100, help="total size of rotated buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--mode", default="lce", choices=["lce", "copy", "traffic"])
+    ap.add_argument("--mode", default="lce", choices=["lce", "copy", "traffic", "rewrite"])
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="--mode traffic: rocprofv3 --pmc output directories")
@@ -242,6 +289,8 @@ def main() -> int:
         ins = base if i == 0 else [t.clone() for t in base]
         Y = torch.empty((cfg.B_c, cfg.M, cfg.D), dtype=tdt, device="cuda")
         sets.append(ins + [Y])
+    if args.mode == "rewrite":
+        return run_rewrite(args, cfg, sets)
     plan = bga.LcePlan(cfg.B_u, cfg.B_c, cfg.K_u, cfg.K_c, cfg.M, cfg.D, dtype=cfg.dtype, variant=args.variant)
     info = plan.info()
     stream = torch.cuda.current_stream()
