@@ -1,4 +1,4 @@
-"""CPU oracle for the IKBO Linear Compression Embedding forward.
+"""CPU oracle for the IKBO Linear Compression Embedding forward and its backward.
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg are the only callers.  The product package never imports this
@@ -7,8 +7,12 @@ module, and this module imports nothing from the product package.
 The arithmetic lives in ``ikbo_oracle.c`` (plain C, fp64): it materialises the
 broadcast ``X_b = [U[map[b]] ; C[b]]`` and computes ``Y[b] = [W_u | W_c] . X_b``
 (IKBO recsys blog, "Deep Dive: Linear Compression": the baseline batched matmul
-and the stage-1 decomposition it equals by linearity).  This wrapper only
-marshals numpy arrays.
+and the stage-1 decomposition it equals by linearity).  The backward is the
+adjoint of that same materialised product, step by step: ``dX_b = W^T dY[b]``,
+whose user rows are scattered back onto ``dU[map[b]]`` (the replication's adjoint)
+and whose candidate rows are ``dC[b]``, and ``dW = sum_b dY[b] X_b^T``.  The pages
+give no training formulas; this is the plain chain rule of the forward they define.
+This wrapper only marshals numpy arrays.
 """
 from __future__ import annotations
 
@@ -52,6 +56,9 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
+        lib.ikbo_oracle_lce_backward_f64.restype = ctypes.c_int
+        lib.ikbo_oracle_lce_backward_f64.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + [
+            ctypes.c_int, ctypes.c_int]
         lib.ikbo_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -108,6 +115,43 @@ def lce_f64(U: np.ndarray, C: np.ndarray, mp: np.ndarray, W_u: np.ndarray, W_c: 
     if st != 0:
         raise OracleError(f"oracle returned {st}")
     return Y
+
+
+def lce_backward_f64(dY: np.ndarray, U: np.ndarray, C: np.ndarray, mp: np.ndarray, W_u: np.ndarray,
+                     W_c: np.ndarray, threads: int = 0):
+    """Gradients of L = <dY, Y> for Y = LCE(U, C, map, W_u, W_c), in fp64.
+
+    Returns (dU [B_u, K_u, D], dC [B_c, K_c, D], dW_u [M, K_u], dW_c [M, K_c]).  dY and
+    the floating inputs share one storage dtype (``uint16`` bf16 bit patterns or
+    ``float32``).  Users that no candidate maps to get dU = 0."""
+    dt = U.dtype
+    if not all(a.dtype == dt for a in (dY, C, W_u, W_c)):
+        raise TypeError("dY, U, C, W_u, W_c must share one dtype")
+    if dt == np.uint16:
+        code = ORACLE_BF16
+    elif dt == np.float32:
+        code = ORACLE_F32
+    else:
+        raise TypeError(f"unsupported dtype {dt}")
+    B_u, K_u, D = U.shape
+    B_c, K_c, D2 = C.shape
+    M, K_u2 = W_u.shape
+    M2, K_c2 = W_c.shape
+    if (D, K_u, K_c, M) != (D2, K_u2, K_c2, M2) or mp.shape != (B_c,) or dY.shape != (B_c, M, D):
+        raise ValueError("inconsistent shapes")
+    dY, U, C, W_u, W_c = (np.ascontiguousarray(a) for a in (dY, U, C, W_u, W_c))
+    mp = np.ascontiguousarray(mp, dtype=np.int32)
+    dU = np.empty((B_u, K_u, D))
+    dC = np.empty((B_c, K_c, D))
+    dW_u = np.empty((M, K_u))
+    dW_c = np.empty((M, K_c))
+    st = _load().ikbo_oracle_lce_backward_f64(
+        dY.ctypes.data, U.ctypes.data, C.ctypes.data, mp.ctypes.data, W_u.ctypes.data, W_c.ctypes.data,
+        dU.ctypes.data, dC.ctypes.data, dW_u.ctypes.data, dW_c.ctypes.data, B_u, B_c, K_u, K_c, M, D,
+        code, int(threads))
+    if st != 0:
+        raise OracleError(f"oracle returned {st}")
+    return dU, dC, dW_u, dW_c
 
 
 def tolerance_violations(Y_gpu: np.ndarray, Y_ref: np.ndarray, atol: float = 1e-3,

@@ -1,5 +1,6 @@
 /*
- * ikbo_oracle.c -- CPU reference for the IKBO Linear Compression Embedding forward.
+ * ikbo_oracle.c -- CPU reference for the IKBO Linear Compression Embedding forward
+ * (and, below, its backward).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  The product path never
@@ -123,6 +124,109 @@ int ikbo_oracle_lce_f64(const void *U, const void *C, const int32_t *map,
         }
         free(X);
         free(acc);
+    }
+    free(W);
+    return status;
+}
+
+/*
+ * Backward of the same materialised product, for an upstream gradient dY [B_c, M, D]
+ * (the pages give no formulas for training; this is the adjoint of the definition
+ * above, taken step by step):
+ *
+ *     dX_b   = W^T . dY[b]                       [K_u + K_c, D]
+ *     dC[b]  = rows K_u.. of dX_b                (the candidate's own rows)
+ *     dU[u] += rows 0..K_u-1 of dX_b  for every b with map[b] = u
+ *                                                (the adjoint of the replication is a
+ *                                                 scatter-add; users with no candidate
+ *                                                 get zero)
+ *     dW     = sum_b dY[b] . X_b^T               [M, K_u + K_c] = [dW_u | dW_c]
+ *
+ * Orders (independent of the thread count): dX_b sums over m ascending; dU adds the
+ * candidates of a user in ascending b; dW sums over b ascending, then d ascending.
+ * Outputs in double: dU [B_u, K_u, D], dC [B_c, K_c, D], dW_u [M, K_u], dW_c [M, K_c].
+ */
+int ikbo_oracle_lce_backward_f64(const void *dY, const void *U, const void *C, const int32_t *map,
+                                 const void *W_u, const void *W_c, double *dU, double *dC,
+                                 double *dW_u, double *dW_c, int64_t B_u, int64_t B_c, int64_t K_u,
+                                 int64_t K_c, int64_t M, int64_t D, int dtype, int nthreads)
+{
+    if (!dY || !U || !C || !map || !W_u || !W_c || !dU || !dC || !dW_u || !dW_c) return ORACLE_ERR_ARG;
+    if (B_u < 1 || B_c < 0 || K_u < 0 || K_c < 0 || M < 1 || D < 1) return ORACLE_ERR_ARG;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F32) return ORACLE_ERR_ARG;
+    for (int64_t b = 0; b < B_c; ++b)
+        if (map[b] < 0 || map[b] >= B_u) return ORACLE_ERR_MAP;
+
+    const int64_t K = K_u + K_c;
+    double *W = (double *)malloc(sizeof(double) * (size_t)(M * (K > 0 ? K : 1)));
+    if (!W) return ORACLE_ERR_NOMEM;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K_u; ++k) W[m * K + k] = widen(W_u, m * K_u + k, dtype);
+        for (int64_t k = 0; k < K_c; ++k) W[m * K + K_u + k] = widen(W_c, m * K_c + k, dtype);
+    }
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int status = ORACLE_OK;
+    memset(dU, 0, sizeof(double) * (size_t)(B_u * K_u * D));
+
+    /* dX_b = W^T dY[b]: candidate rows into dC[b]; user rows added into dU[map[b]], the
+     * candidates of one user taken in ascending b by the thread that owns that user. */
+#pragma omp parallel
+    {
+        double *dX = (double *)malloc(sizeof(double) * (size_t)((K > 0 ? K : 1) * D));
+        if (!dX) {
+#pragma omp atomic write
+            status = ORACLE_ERR_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t b = 0; b < B_c; ++b) {
+                for (int64_t k = K_u; k < K; ++k) {
+                    double *out = dC + (b * K_c + (k - K_u)) * D;
+                    for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+                    for (int64_t m = 0; m < M; ++m) {
+                        const double w = W[m * K + k];
+                        for (int64_t d = 0; d < D; ++d) out[d] += w * widen(dY, (b * M + m) * D + d, dtype);
+                    }
+                }
+            }
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t u = 0; u < B_u; ++u) {
+                for (int64_t b = 0; b < B_c; ++b) {
+                    if (map[b] != u) continue;
+                    for (int64_t k = 0; k < K_u; ++k) {
+                        double *x = dX + k * D;
+                        for (int64_t d = 0; d < D; ++d) x[d] = 0.0;
+                        for (int64_t m = 0; m < M; ++m) {
+                            const double w = W[m * K + k];
+                            for (int64_t d = 0; d < D; ++d) x[d] += w * widen(dY, (b * M + m) * D + d, dtype);
+                        }
+                        double *acc = dU + (u * K_u + k) * D;
+                        for (int64_t d = 0; d < D; ++d) acc[d] += x[d];
+                    }
+                }
+            }
+        }
+        free(dX);
+    }
+
+    /* dW[m][k] = sum over b (ascending), then d (ascending), of dY[b][m][d] * X_b[k][d]. */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < B_c; ++b) {
+                for (int64_t d = 0; d < D; ++d) {
+                    const double x = k < K_u ? widen(U, ((int64_t)map[b] * K_u + k) * D + d, dtype)
+                                             : widen(C, (b * K_c + (k - K_u)) * D + d, dtype);
+                    acc += widen(dY, (b * M + m) * D + d, dtype) * x;
+                }
+            }
+            if (k < K_u) dW_u[m * K_u + k] = acc;
+            else dW_c[m * K_c + (k - K_u)] = acc;
+        }
     }
     free(W);
     return status;
