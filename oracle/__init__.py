@@ -57,8 +57,8 @@ def _load():
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
         lib.ikbo_oracle_lce_backward_f64.restype = ctypes.c_int
-        lib.ikbo_oracle_lce_backward_f64.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + [
-            ctypes.c_int, ctypes.c_int]
+        lib.ikbo_oracle_lce_backward_f64.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 6 + [
+            ctypes.c_int] + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p] * 3 + [ctypes.c_int]
         lib.ikbo_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -117,13 +117,7 @@ def lce_f64(U: np.ndarray, C: np.ndarray, mp: np.ndarray, W_u: np.ndarray, W_c: 
     return Y
 
 
-def lce_backward_f64(dY: np.ndarray, U: np.ndarray, C: np.ndarray, mp: np.ndarray, W_u: np.ndarray,
-                     W_c: np.ndarray, threads: int = 0):
-    """Gradients of L = <dY, Y> for Y = LCE(U, C, map, W_u, W_c), in fp64.
-
-    Returns (dU [B_u, K_u, D], dC [B_c, K_c, D], dW_u [M, K_u], dW_c [M, K_c]).  dY and
-    the floating inputs share one storage dtype (``uint16`` bf16 bit patterns or
-    ``float32``).  Users that no candidate maps to get dU = 0."""
+def _check_backward_args(dY, U, C, mp, W_u, W_c):
     dt = U.dtype
     if not all(a.dtype == dt for a in (dY, C, W_u, W_c)):
         raise TypeError("dY, U, C, W_u, W_c must share one dtype")
@@ -139,19 +133,49 @@ def lce_backward_f64(dY: np.ndarray, U: np.ndarray, C: np.ndarray, mp: np.ndarra
     M2, K_c2 = W_c.shape
     if (D, K_u, K_c, M) != (D2, K_u2, K_c2, M2) or mp.shape != (B_c,) or dY.shape != (B_c, M, D):
         raise ValueError("inconsistent shapes")
+    return code, (B_u, B_c, K_u, K_c, M, D)
+
+
+def _pairs(x) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int64).reshape(-1, 2))
+    return a
+
+
+def lce_backward_rows_f64(dY: np.ndarray, U: np.ndarray, C: np.ndarray, mp: np.ndarray, W_u: np.ndarray,
+                          W_c: np.ndarray, dc_rows=(), du_rows=(), dw_elems=(), threads: int = 0):
+    """Sampled gradients of L = <dY, Y> for Y = LCE(U, C, map, W_u, W_c), in fp64.
+
+    dc_rows: (b, k) pairs -> dC[b, k, :]; du_rows: (u, k) pairs -> dU[u, k, :];
+    dw_elems: (m, kk) pairs -> dW_u[m, kk] for kk < K_u, else dW_c[m, kk - K_u].
+    Returns (dC_rows [n, D], dU_rows [n, D], dW [n]).  dY and the floating inputs share
+    one storage dtype (``uint16`` bf16 bit patterns or ``float32``)."""
+    code, (B_u, B_c, K_u, K_c, M, D) = _check_backward_args(dY, U, C, mp, W_u, W_c)
     dY, U, C, W_u, W_c = (np.ascontiguousarray(a) for a in (dY, U, C, W_u, W_c))
     mp = np.ascontiguousarray(mp, dtype=np.int32)
-    dU = np.empty((B_u, K_u, D))
-    dC = np.empty((B_c, K_c, D))
-    dW_u = np.empty((M, K_u))
-    dW_c = np.empty((M, K_c))
+    pc, pu, pw = _pairs(dc_rows), _pairs(du_rows), _pairs(dw_elems)
+    oc, ou, ow = np.empty((len(pc), D)), np.empty((len(pu), D)), np.empty(len(pw))
     st = _load().ikbo_oracle_lce_backward_f64(
         dY.ctypes.data, U.ctypes.data, C.ctypes.data, mp.ctypes.data, W_u.ctypes.data, W_c.ctypes.data,
-        dU.ctypes.data, dC.ctypes.data, dW_u.ctypes.data, dW_c.ctypes.data, B_u, B_c, K_u, K_c, M, D,
-        code, int(threads))
+        B_u, B_c, K_u, K_c, M, D, code,
+        pc.ctypes.data, len(pc), oc.ctypes.data, pu.ctypes.data, len(pu), ou.ctypes.data,
+        pw.ctypes.data, len(pw), ow.ctypes.data, int(threads))
     if st != 0:
         raise OracleError(f"oracle returned {st}")
-    return dU, dC, dW_u, dW_c
+    return oc, ou, ow
+
+
+def lce_backward_f64(dY: np.ndarray, U: np.ndarray, C: np.ndarray, mp: np.ndarray, W_u: np.ndarray,
+                     W_c: np.ndarray, threads: int = 0):
+    """All gradients: (dU [B_u, K_u, D], dC [B_c, K_c, D], dW_u [M, K_u], dW_c [M, K_c]).
+
+    Users that no candidate maps to get dU = 0."""
+    _, (B_u, B_c, K_u, K_c, M, D) = _check_backward_args(dY, U, C, mp, W_u, W_c)
+    grid = lambda a, b: np.stack(np.meshgrid(np.arange(a), np.arange(b), indexing="ij"), -1).reshape(-1, 2)
+    oc, ou, ow = lce_backward_rows_f64(dY, U, C, mp, W_u, W_c, grid(B_c, K_c), grid(B_u, K_u),
+                                       grid(M, K_u + K_c), threads)
+    dW = ow.reshape(M, K_u + K_c)
+    return (ou.reshape(B_u, K_u, D), oc.reshape(B_c, K_c, D), np.ascontiguousarray(dW[:, :K_u]),
+            np.ascontiguousarray(dW[:, K_u:]))
 
 
 def tolerance_violations(Y_gpu: np.ndarray, Y_ref: np.ndarray, atol: float = 1e-3,

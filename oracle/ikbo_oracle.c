@@ -136,28 +136,44 @@ int ikbo_oracle_lce_f64(const void *U, const void *C, const int32_t *map,
  *
  *     dX_b   = W^T . dY[b]                       [K_u + K_c, D]
  *     dC[b]  = rows K_u.. of dX_b                (the candidate's own rows)
- *     dU[u] += rows 0..K_u-1 of dX_b  for every b with map[b] = u
+ *     dU[u]  = sum over b with map[b] = u of rows 0..K_u-1 of dX_b
  *                                                (the adjoint of the replication is a
  *                                                 scatter-add; users with no candidate
  *                                                 get zero)
  *     dW     = sum_b dY[b] . X_b^T               [M, K_u + K_c] = [dW_u | dW_c]
  *
- * Orders (independent of the thread count): dX_b sums over m ascending; dU adds the
- * candidates of a user in ascending b; dW sums over b ascending, then d ascending.
- * Outputs in double: dU [B_u, K_u, D], dC [B_c, K_c, D], dW_u [M, K_u], dW_c [M, K_c].
+ * Only the requested outputs are computed, so that large batches can be checked on a
+ * sample: dC rows (b, k) and dU rows (u, k) give D values each, dW elements (m, kk)
+ * with kk < K_u in dW_u and kk >= K_u in dW_c (column kk - K_u) give one value each.
+ * Orders (independent of the thread count): a row of dX_b sums over m ascending; a dU
+ * row adds the candidates of its user in ascending b; a dW element sums over b
+ * ascending, then d ascending.
  */
 int ikbo_oracle_lce_backward_f64(const void *dY, const void *U, const void *C, const int32_t *map,
-                                 const void *W_u, const void *W_c, double *dU, double *dC,
-                                 double *dW_u, double *dW_c, int64_t B_u, int64_t B_c, int64_t K_u,
-                                 int64_t K_c, int64_t M, int64_t D, int dtype, int nthreads)
+                                 const void *W_u, const void *W_c, int64_t B_u, int64_t B_c, int64_t K_u,
+                                 int64_t K_c, int64_t M, int64_t D, int dtype,
+                                 const int64_t *dc_rows, int64_t n_dc, double *dC,
+                                 const int64_t *du_rows, int64_t n_du, double *dU,
+                                 const int64_t *dw_elems, int64_t n_dw, double *dW, int nthreads)
 {
-    if (!dY || !U || !C || !map || !W_u || !W_c || !dU || !dC || !dW_u || !dW_c) return ORACLE_ERR_ARG;
+    if (!dY || !U || !C || !map || !W_u || !W_c) return ORACLE_ERR_ARG;
+    if ((n_dc && (!dc_rows || !dC)) || (n_du && (!du_rows || !dU)) || (n_dw && (!dw_elems || !dW)))
+        return ORACLE_ERR_ARG;
     if (B_u < 1 || B_c < 0 || K_u < 0 || K_c < 0 || M < 1 || D < 1) return ORACLE_ERR_ARG;
     if (dtype != ORACLE_BF16 && dtype != ORACLE_F32) return ORACLE_ERR_ARG;
     for (int64_t b = 0; b < B_c; ++b)
         if (map[b] < 0 || map[b] >= B_u) return ORACLE_ERR_MAP;
-
     const int64_t K = K_u + K_c;
+    for (int64_t i = 0; i < n_dc; ++i)
+        if (dc_rows[2 * i] < 0 || dc_rows[2 * i] >= B_c || dc_rows[2 * i + 1] < 0 || dc_rows[2 * i + 1] >= K_c)
+            return ORACLE_ERR_ARG;
+    for (int64_t i = 0; i < n_du; ++i)
+        if (du_rows[2 * i] < 0 || du_rows[2 * i] >= B_u || du_rows[2 * i + 1] < 0 || du_rows[2 * i + 1] >= K_u)
+            return ORACLE_ERR_ARG;
+    for (int64_t i = 0; i < n_dw; ++i)
+        if (dw_elems[2 * i] < 0 || dw_elems[2 * i] >= M || dw_elems[2 * i + 1] < 0 || dw_elems[2 * i + 1] >= K)
+            return ORACLE_ERR_ARG;
+
     double *W = (double *)malloc(sizeof(double) * (size_t)(M * (K > 0 ? K : 1)));
     if (!W) return ORACLE_ERR_NOMEM;
     for (int64_t m = 0; m < M; ++m) {
@@ -170,63 +186,59 @@ int ikbo_oracle_lce_backward_f64(const void *dY, const void *U, const void *C, c
     (void)nthreads;
 #endif
     int status = ORACLE_OK;
-    memset(dU, 0, sizeof(double) * (size_t)(B_u * K_u * D));
 
-    /* dX_b = W^T dY[b]: candidate rows into dC[b]; user rows added into dU[map[b]], the
-     * candidates of one user taken in ascending b by the thread that owns that user. */
+    /* dC rows: row K_u + k of dX_b. */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_dc; ++i) {
+        const int64_t b = dc_rows[2 * i], k = K_u + dc_rows[2 * i + 1];
+        double *out = dC + i * D;
+        for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+        for (int64_t m = 0; m < M; ++m) {
+            const double w = W[m * K + k];
+            for (int64_t d = 0; d < D; ++d) out[d] += w * widen(dY, (b * M + m) * D + d, dtype);
+        }
+    }
+
+    /* dU rows: row k of dX_b, added over the user's candidates in ascending b. */
 #pragma omp parallel
     {
-        double *dX = (double *)malloc(sizeof(double) * (size_t)((K > 0 ? K : 1) * D));
-        if (!dX) {
+        double *x = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!x) {
 #pragma omp atomic write
             status = ORACLE_ERR_NOMEM;
         } else {
 #pragma omp for schedule(dynamic, 1)
-            for (int64_t b = 0; b < B_c; ++b) {
-                for (int64_t k = K_u; k < K; ++k) {
-                    double *out = dC + (b * K_c + (k - K_u)) * D;
-                    for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
-                    for (int64_t m = 0; m < M; ++m) {
-                        const double w = W[m * K + k];
-                        for (int64_t d = 0; d < D; ++d) out[d] += w * widen(dY, (b * M + m) * D + d, dtype);
-                    }
-                }
-            }
-#pragma omp for schedule(dynamic, 1)
-            for (int64_t u = 0; u < B_u; ++u) {
+            for (int64_t i = 0; i < n_du; ++i) {
+                const int64_t u = du_rows[2 * i], k = du_rows[2 * i + 1];
+                double *acc = dU + i * D;
+                for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
                 for (int64_t b = 0; b < B_c; ++b) {
                     if (map[b] != u) continue;
-                    for (int64_t k = 0; k < K_u; ++k) {
-                        double *x = dX + k * D;
-                        for (int64_t d = 0; d < D; ++d) x[d] = 0.0;
-                        for (int64_t m = 0; m < M; ++m) {
-                            const double w = W[m * K + k];
-                            for (int64_t d = 0; d < D; ++d) x[d] += w * widen(dY, (b * M + m) * D + d, dtype);
-                        }
-                        double *acc = dU + (u * K_u + k) * D;
-                        for (int64_t d = 0; d < D; ++d) acc[d] += x[d];
+                    for (int64_t d = 0; d < D; ++d) x[d] = 0.0;
+                    for (int64_t m = 0; m < M; ++m) {
+                        const double w = W[m * K + k];
+                        for (int64_t d = 0; d < D; ++d) x[d] += w * widen(dY, (b * M + m) * D + d, dtype);
                     }
+                    for (int64_t d = 0; d < D; ++d) acc[d] += x[d];
                 }
             }
         }
-        free(dX);
+        free(x);
     }
 
-    /* dW[m][k] = sum over b (ascending), then d (ascending), of dY[b][m][d] * X_b[k][d]. */
+    /* dW[m][kk] = sum over b (ascending), then d (ascending), of dY[b][m][d] * X_b[kk][d]. */
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t m = 0; m < M; ++m) {
-        for (int64_t k = 0; k < K; ++k) {
-            double acc = 0.0;
-            for (int64_t b = 0; b < B_c; ++b) {
-                for (int64_t d = 0; d < D; ++d) {
-                    const double x = k < K_u ? widen(U, ((int64_t)map[b] * K_u + k) * D + d, dtype)
-                                             : widen(C, (b * K_c + (k - K_u)) * D + d, dtype);
-                    acc += widen(dY, (b * M + m) * D + d, dtype) * x;
-                }
+    for (int64_t i = 0; i < n_dw; ++i) {
+        const int64_t m = dw_elems[2 * i], k = dw_elems[2 * i + 1];
+        double acc = 0.0;
+        for (int64_t b = 0; b < B_c; ++b) {
+            for (int64_t d = 0; d < D; ++d) {
+                const double x = k < K_u ? widen(U, ((int64_t)map[b] * K_u + k) * D + d, dtype)
+                                         : widen(C, (b * K_c + (k - K_u)) * D + d, dtype);
+                acc += widen(dY, (b * M + m) * D + d, dtype) * x;
             }
-            if (k < K_u) dW_u[m * K_u + k] = acc;
-            else dW_c[m * K_c + (k - K_u)] = acc;
         }
+        dW[i] = acc;
     }
     free(W);
     return status;
