@@ -1,4 +1,4 @@
-"""broadcast_gemm_amd -- IKBO Linear Compression Embedding forward for AMD MI355X.
+"""broadcast_gemm_amd -- IKBO Linear Compression Embedding forward (and backward) for AMD MI355X.
 
     Y[b] = W_u . U[map[b]] + W_c . C[b]
 
@@ -9,6 +9,9 @@ if the library is not built, every call raises.
 
     plan = LcePlan(max_B_u, max_B_c, K_u, K_c, M, D, dtype="bf16", variant="S4")
     Y = plan.forward(U, C, map, W_u, W_c)        # torch tensors on the GPU
+
+    plan = LcePlan(..., flags=FLAG_BACKWARD)     # the backward's workspace as well
+    dU, dC, dW_u, dW_c = plan.backward(dY, U, C, map, W_u, W_c)
 """
 from __future__ import annotations
 
@@ -32,9 +35,10 @@ DTYPES = {"bf16": 0, "f32": 1}
 VARIANTS = {"auto": 0, "S0": 1, "S1": 2, "S2": 3, "S3": 4, "S4": 5}
 FLAG_DEBUG_DELAY_USER = 2
 FLAG_DEBUG_SKIP_USER = 4
+FLAG_BACKWARD = 8
 
 # Every symbol include/ikbo.h declares.
-EXPORTED = ("ikbo_lce_plan", "ikbo_lce_forward", "ikbo_lce_check", "ikbo_lce_plan_info",
+EXPORTED = ("ikbo_lce_plan", "ikbo_lce_forward", "ikbo_lce_backward", "ikbo_lce_check", "ikbo_lce_plan_info",
             "ikbo_lce_plan_set_spin_limit", "ikbo_lce_plan_destroy", "ikbo_status_str",
             "ikbo_last_error_message")
 
@@ -64,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.ikbo_lce_plan.restype = ip
         L.ikbo_lce_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
         L.ikbo_lce_forward.restype = ip
+        L.ikbo_lce_backward.argtypes = [vp] + [vp] * 10 + [i] * 6 + [vp]
+        L.ikbo_lce_backward.restype = ip
         L.ikbo_lce_check.argtypes = [vp, vp]
         L.ikbo_lce_check.restype = ip
         L.ikbo_lce_plan_info.argtypes = [vp, ctypes.c_char_p, sz]
@@ -165,6 +171,48 @@ class LcePlan:
                                out.data_ptr(), B_u, B_c, _stream_handle(stream))
         if st != IKBO_OK:
             raise IkboError(st, "ikbo_lce_forward")
+        return out
+
+    def backward_ptrs(self, dY: int, U: int, C: int, mp: int, W_u: int, W_c: int, dU: int, dC: int,
+                      dW_u: int, dW_c: int, B_u: int, B_c: int, stream: Optional[int] = None) -> int:
+        """Raw C-ABI call on device pointers; returns the status code."""
+        K_u, K_c, M, D = self.dims
+        return lib().ikbo_lce_backward(self.handle, dY, U, C, mp, W_u, W_c, dU, dC, dW_u, dW_c,
+                                       B_u, B_c, K_u, K_c, M, D, stream)
+
+    def backward(self, dY, U, C, mp, W_u, W_c, out=None, stream=None):
+        """Gradients (dU, dC, dW_u, dW_c) of <dY, Y> on the current (or given) stream.
+
+        Needs a plan made with ``flags=FLAG_BACKWARD``.  dU and dC come back in the plan's
+        dtype (bf16), dW_u and dW_c in float32.  ``out`` may supply the four tensors."""
+        torch = _torch()
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        for name, t in (("dY", dY), ("U", U), ("C", C), ("W_u", W_u), ("W_c", W_c)):
+            if t.dtype != tdt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {tdt} tensor on the GPU")
+        if mp.dtype != torch.int32:
+            mp = mp.to(torch.int32)
+        mp = mp.contiguous()
+        K_u, K_c, M, D = self.dims
+        B_u, B_c = U.shape[0], C.shape[0]
+        if tuple(U.shape) != (B_u, K_u, D) or tuple(C.shape) != (B_c, K_c, D) or tuple(dY.shape) != (B_c, M, D) \
+                or tuple(W_u.shape) != (M, K_u) or tuple(W_c.shape) != (M, K_c) or mp.shape != (B_c,):
+            raise IkboError(IKBO_ERR_INVALID_ARG, "shape differs from the plan")
+        shapes = ((B_u, K_u, D), (B_c, K_c, D), (M, K_u), (M, K_c))
+        dts = (tdt, tdt, torch.float32, torch.float32)
+        if out is None:
+            out = tuple(torch.empty(sh, dtype=dt, device=U.device) for sh, dt in zip(shapes, dts))
+        else:
+            out = tuple(out)
+            for t, sh, dt in zip(out, shapes, dts):
+                if t.dtype != dt or not t.is_contiguous() or tuple(t.shape) != sh:
+                    raise ValueError("out must be (dU, dC, dW_u, dW_c) contiguous tensors of the gradient shapes")
+        dU, dC, dW_u, dW_c = out
+        st = self.backward_ptrs(dY.data_ptr(), U.data_ptr(), C.data_ptr(), mp.data_ptr(), W_u.data_ptr(),
+                                W_c.data_ptr(), dU.data_ptr(), dC.data_ptr(), dW_u.data_ptr(), dW_c.data_ptr(),
+                                B_u, B_c, _stream_handle(stream))
+        if st != IKBO_OK:
+            raise IkboError(st, "ikbo_lce_backward")
         return out
 
     def check(self, stream=None) -> int:

@@ -49,6 +49,16 @@ struct ikbo_lce_plan_s {
     int ksplit, ks_per_split;
     uint32_t spin_limit;
     uint32_t epoch;                 // last epoch handed to a same-launch user/candidate forward
+    // backward (IKBO_FLAG_BACKWARD)
+    int bwd;
+    int dc_mb, dc_nmc, dc_mpad, dc_bpc;   // dC on the row-tile engine: K_c output rows, K = M
+    TileConfig du_tile;                   // dU on the flat engine: K_u output rows, K = 2M
+    int du_nmc, du_ldw;
+    int seg_T, seg_slices;                // segment sums: most chunks, 512-element slices
+    int wgc_chunks, wgu_chunks;           // most entry chunks of the dW_c and dW_u products
+    uint16_t *Wt_c, *W_dup, *S2;
+    int32_t *perm, *su, *off;
+    float *seg_part, *part_c, *part_u;
     // workspace (one hipMalloc arena)
     char *arena;
     size_t arena_bytes;
@@ -115,7 +125,8 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     if (max_B_u < 1 || max_B_c < 0 || K_u < 1 || K_c < 1 || M < 1 || D < 1) return IKBO_ERR_INVALID_ARG;
     if (dtype != IKBO_DTYPE_BF16 && dtype != IKBO_DTYPE_F32) return IKBO_ERR_INVALID_ARG;
     if (variant < IKBO_VARIANT_AUTO || variant > IKBO_S4_PERSISTENT) return IKBO_ERR_INVALID_ARG;
-    if (flags & ~(unsigned)(IKBO_FLAG_DEBUG_DELAY_USER | IKBO_FLAG_DEBUG_SKIP_USER)) return IKBO_ERR_INVALID_ARG;
+    if (flags & ~(unsigned)(IKBO_FLAG_DEBUG_DELAY_USER | IKBO_FLAG_DEBUG_SKIP_USER | IKBO_FLAG_BACKWARD))
+        return IKBO_ERR_INVALID_ARG;
     if (variant == IKBO_VARIANT_AUTO) variant = IKBO_S4_PERSISTENT;
     const int elt = dtype == IKBO_DTYPE_BF16 ? 2 : 4;
     // Rows of D elements must be whole 16-byte chunks (128-bit loads and stores).
@@ -124,6 +135,9 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     if ((long long)max_B_c * D >= (1LL << 40) || (long long)K_u + K_c > (1 << 24) || M > (1 << 20) ||
         (long long)(K_u + K_c) * D * elt >= (1LL << 31))
         return IKBO_ERR_UNSUPPORTED;
+
+    // The backward runs on the row-tile engine's column layouts, in bf16 only.
+    if ((flags & IKBO_FLAG_BACKWARD) && (dtype != IKBO_DTYPE_BF16 || !rows_supported(D))) return IKBO_ERR_UNSUPPORTED;
 
     ikbo_lce_plan_s *p = new (std::nothrow) ikbo_lce_plan_s();
     if (p == nullptr) return IKBO_ERR_INVALID_ARG;
@@ -190,6 +204,43 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     p->ksplit = ceil_div(n_ks_u, p->ks_per_split);
     p->n_ucols_max = (int)(((long long)max_B_u * D + 127) / 128);
 
+    // ---- backward geometry ----
+    if (flags & IKBO_FLAG_BACKWARD) {
+        // bf16 with a row-tile column layout; every 2-D extent's byte size stays in 31 bits.
+        if ((long long)std::max(2 * M, std::max(K_u, K_c)) * D * 2 >= (1LL << 31) ||
+            (long long)M * std::max(K_u, K_c) * 2 * 4 >= (1LL << 31)) {
+            delete p;
+            return IKBO_ERR_UNSUPPORTED;
+        }
+        p->bwd = 1;
+        const int nmb_c = ceil_div(K_c, 16);
+        p->dc_mb = std::max(1, std::min(env_int("IKBO_BWD_DC_MB", rows_max_mb(D)), rows_max_mb(D)));
+        p->dc_nmc = ceil_div(nmb_c, p->dc_mb);
+        p->dc_mpad = p->dc_nmc * p->dc_mb * 16;
+        const size_t lds_t = (size_t)lds_w_elems(K_c, M) * 2;
+        p->dc_bpc = lds_t <= (size_t)max_lds ? rows_blocks_per_cu(EPI_STORE_T, D, p->dc_mb, lds_t) : 0;
+        const int nmb_u = ceil_div(K_u, 16);
+        p->du_tile.vec = 8;
+        p->du_tile.packed = true;
+        p->du_tile.mb = choose_mb(nmb_u, 4);
+        p->du_nmc = ceil_div(nmb_u, p->du_tile.mb);
+        p->du_tile.wpb = std::min(p->du_nmc, 4);
+        p->du_ldw = ceil_div(2 * M, 32) * 32;
+        const int slices = ceil_div(M * D, 512);
+        p->seg_slices = slices;
+        const int seg_waves = std::max(64, env_int("IKBO_BWD_SEG_WAVES", 2048));
+        // Chunks of the sorted candidate list: at most seg_T, sized from the call's B_c (so the
+        // summation order, and with it every bit of S, does not depend on the plan's capacity).
+        p->seg_T = std::max(1, seg_waves / slices);
+        p->wgc_chunks = std::max(1, std::min(env_int("IKBO_BWD_WGC_CHUNKS", 128), std::max(max_B_c, 1)));
+        p->wgu_chunks = std::max(1, std::min(8, max_B_u));
+        if (p->dc_bpc < 1 || (long long)p->dc_mpad * D * 4 >= (1LL << 31) ||
+            bwd_prep_lds_bytes(max_B_u, max_B_c) > (size_t)std::min(max_lds, 64 * 1024)) {
+            delete p;
+            return IKBO_ERR_UNSUPPORTED;
+        }
+    }
+
     // ---- workspace ----
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes, 256); return at; };
@@ -219,6 +270,19 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
         if (flat && variant == IKBO_S4_PERSISTENT && p->ksplit > 1)
             o_part = take((size_t)(p->ksplit - 1) * pu_bytes);
     }
+    size_t o_wtc = 0, o_wdup = 0, o_perm = 0, o_su = 0, o_off = 0, o_seg = 0, o_s2 = 0, o_bpc = 0, o_pu2 = 0;
+    if (p->bwd) {
+        const size_t MD = (size_t)M * D;
+        o_wtc = take((size_t)K_c * M * 2);
+        o_wdup = take((size_t)p->du_nmc * p->du_tile.mb * 16 * p->du_ldw * 2);
+        o_perm = take((size_t)std::max(max_B_c, 1) * 4);
+        o_su = take((size_t)std::max(max_B_c, 1) * 4);
+        o_off = take((size_t)(max_B_u + 1) * 4);
+        o_seg = take((size_t)(p->seg_T + max_B_u) * MD * 4);
+        o_s2 = take((size_t)max_B_u * 2 * MD * 2);
+        o_bpc = take((size_t)p->wgc_chunks * M * K_c * 4);
+        o_pu2 = take((size_t)p->wgu_chunks * 2 * M * K_u * 4);
+    }
     p->arena_bytes = off;
     e = hipMalloc(reinterpret_cast<void **>(&p->arena), p->arena_bytes);
     if (e != hipSuccess) { delete p; return hip_fail(e, "hipMalloc(workspace)"); }
@@ -237,6 +301,17 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     p->P_c = o_pc ? reinterpret_cast<float *>(A + o_pc) : nullptr;
     p->P_b = o_pb ? reinterpret_cast<float *>(A + o_pb) : nullptr;
     p->P_part = o_part ? reinterpret_cast<float *>(A + o_part) : nullptr;
+    if (p->bwd) {
+        p->Wt_c = reinterpret_cast<uint16_t *>(A + o_wtc);
+        p->W_dup = reinterpret_cast<uint16_t *>(A + o_wdup);
+        p->perm = reinterpret_cast<int32_t *>(A + o_perm);
+        p->su = reinterpret_cast<int32_t *>(A + o_su);
+        p->off = reinterpret_cast<int32_t *>(A + o_off);
+        p->seg_part = reinterpret_cast<float *>(A + o_seg);
+        p->S2 = reinterpret_cast<uint16_t *>(A + o_s2);
+        p->part_c = reinterpret_cast<float *>(A + o_bpc);
+        p->part_u = reinterpret_cast<float *>(A + o_pu2);
+    }
     // Epoch starts at 1 so that the zeroed flags read as "not yet published".
     const uint32_t one = 1;
     e = hipMemcpy(p->state, &one, sizeof one, hipMemcpyHostToDevice);
@@ -297,18 +372,19 @@ int ikbo_lce_plan_info(ikbo_lce_plan_t p, char *json, size_t cap) {
     if (p == nullptr || (json == nullptr && cap > 0)) return IKBO_ERR_INVALID_ARG;
     static const char *names[] = {"AUTO", "S0", "S1", "S2", "S3", "S4"};
     const bool rows = p->engine == ENGINE_ROWS;
-    char buf[1024];
+    char buf[1536];
     int n = snprintf(buf, sizeof buf,
                      "{\"variant\":\"%s\",\"dtype\":\"%s\",\"engine\":\"%s\",\"max_B_u\":%d,\"max_B_c\":%d,"
                      "\"K_u\":%d,\"K_c\":%d,\"M\":%d,\"D\":%d,\"mb\":%d,\"n_mchunks\":%d,\"M_pad\":%d,"
                      "\"vec\":%d,\"K_u_pad\":%d,\"K_c_pad\":%d,\"K_cat_pad\":%d,\"user_ksplit\":%d,"
                      "\"user_ksteps_per_split\":%d,\"blocks_per_cu\":[%d,%d,%d],\"fused_grid\":%d,"
-                     "\"n_cu\":%d,\"workspace_bytes\":%zu}",
+                     "\"n_cu\":%d,\"workspace_bytes\":%zu,\"backward\":%d,\"bwd_dc_mb\":%d,"
+                     "\"bwd_du_mb\":%d,\"bwd_seg_chunks\":%d,\"bwd_wgc_chunks\":%d,\"bwd_wgu_chunks\":%d}",
                      names[p->variant], p->dtype == IKBO_DTYPE_BF16 ? "bf16" : "f32", rows ? "rows" : "flat",
                      p->max_B_u, p->max_B_c, p->K_u, p->K_c, p->M, p->D, rows ? p->rows_mb : p->tile.mb,
                      p->n_mchunks, p->M_pad, rows ? 0 : p->tile.vec, p->ldw_u, p->ldw_c, p->ldw_cat, p->ksplit,
                      p->ks_per_split, p->bpc_user, p->bpc_cand, p->bpc_both, p->fused_grid, p->n_cu,
-                     p->arena_bytes);
+                     p->arena_bytes, p->bwd, p->dc_mb, p->du_tile.mb, p->seg_T, p->wgc_chunks, p->wgu_chunks);
     if (n < 0) return IKBO_ERR_INVALID_ARG;
     if (cap > 0) {
         size_t c = std::min((size_t)n, cap - 1);
@@ -548,6 +624,101 @@ int ikbo_lce_forward(ikbo_lce_plan_t p, const void *U, const void *C, const int3
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (p->engine == ENGINE_ROWS) return forward_rows(p, U, C, map, W_u, W_c, Y, B_u, B_c, s);
     return forward_flat(p, U, C, map, W_u, W_c, Y, B_u, B_c, s);
+}
+
+int ikbo_lce_backward(ikbo_lce_plan_t p, const void *dY, const void *U, const void *C, const int32_t *map,
+                      const void *W_u, const void *W_c, void *dU, void *dC, float *dW_u, float *dW_c,
+                      int B_u, int B_c, int K_u, int K_c, int M, int D, void *stream) {
+    if (p == nullptr || !p->bwd) return IKBO_ERR_INVALID_ARG;
+    if (K_u != p->K_u || K_c != p->K_c || M != p->M || D != p->D) return IKBO_ERR_INVALID_ARG;
+    if (B_c < 0 || B_c > p->max_B_c || B_u < 1 || B_u > p->max_B_u) return IKBO_ERR_INVALID_ARG;
+    if (!U || !W_u || !W_c || !dU || !dW_u || !dW_c || (B_c > 0 && (!dY || !C || !map || !dC)))
+        return IKBO_ERR_INVALID_ARG;
+    if (!aligned16(dU) || !aligned16(U) || !aligned16(W_u) || !aligned16(W_c) || !aligned16(dW_u) ||
+        !aligned16(dW_c) || (B_c > 0 && (!aligned16(dY) || !aligned16(C) || !aligned16(dC) ||
+                                         (reinterpret_cast<uintptr_t>(map) & 3u) != 0)))
+        return IKBO_ERR_ALIGNMENT;
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != p->device) return IKBO_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int MD = M * D;
+
+    // Candidates grouped by user; W_c^T and [W_u^T | W_u^T].
+    BwdPrepArgs pa{};
+    pa.map = map; pa.perm = p->perm; pa.su = p->su; pa.off = p->off; pa.err = p->err;
+    pa.W_u = static_cast<const uint16_t *>(W_u); pa.W_c = static_cast<const uint16_t *>(W_c);
+    pa.Wt_c = p->Wt_c; pa.W_dup = p->W_dup;
+    pa.B_u = B_u; pa.B_c = B_c; pa.M = M; pa.K_u = K_u; pa.K_c = K_c; pa.ldw_dup = p->du_ldw;
+    if ((e = launch_bwd_prep(pa, s)) != hipSuccess) return hip_fail(e, "bwd prep");
+
+    // dC[b] = W_c^T . dY[b] on the row-tile engine (W_c^T staged in LDS).
+    if (B_c > 0) {
+        RowArgs c{};
+        c.C = static_cast<const uint16_t *>(dY);
+        c.W_c = p->Wt_c;
+        c.map = map; c.err = p->err; c.flags = p->flagw; c.P_u = p->P_u;
+        c.out = dC;
+        c.B_u = B_u; c.M = K_c; c.D = D; c.M_pad = p->dc_mpad;
+        c.K_u = 0; c.K_c = M; c.K_wc = M;
+        c.n_ks_u = 0; c.n_ks_c = ceil_div(M, 32);
+        c.n_mchunks = p->dc_nmc; c.n_mblocks = ceil_div(K_c, 16);
+        c.n_user = 0; c.n_cand = B_c * p->dc_nmc;
+        c.spin_limit = p->spin_limit;
+        const int grid = std::max(1, std::min(p->n_cu * p->dc_bpc, ceil_div(c.n_cand, kRowsBlock / 64)));
+        if (rows_lds_bytes(c) > (size_t)p->max_lds) return IKBO_ERR_UNSUPPORTED;
+        if ((e = launch_rows(EPI_STORE_T, p->dc_mb, c, grid, s)) != hipSuccess) return hip_fail(e, "bwd dC");
+    }
+
+    // dW_c partials: sum over candidates of dY[b] . C[b]^T.
+    WgradArgs wc{};
+    int P_c = 0;
+    if (B_c > 0) {
+        wc.A = static_cast<const uint16_t *>(dY); wc.B = static_cast<const uint16_t *>(C); wc.part = p->part_c;
+        wc.E = B_c; wc.R = M; wc.N = K_c; wc.D = D;
+        wc.per_chunk = ceil_div(B_c, p->wgc_chunks);
+        wc.n_chunks = P_c = ceil_div(B_c, wc.per_chunk);
+        wc.n_rt = ceil_div(ceil_div(M, 16), kWgradMR);
+        wc.n_nt = ceil_div(ceil_div(K_c, 16), kWgradNC);
+        wc.tgroups = ceil_div(wc.n_rt * wc.n_nt, 4);
+        if ((e = launch_wgrad(wc, s)) != hipSuccess) return hip_fail(e, "bwd dW_c");
+    }
+
+    // S[u] = sum of dY over the user's candidates, as [bf16(S); bf16(S - hi)].
+    SegsumArgs sa{};
+    sa.dY = static_cast<const uint16_t *>(dY); sa.perm = p->perm; sa.su = p->su; sa.off = p->off;
+    sa.part = p->seg_part; sa.S2 = p->S2;
+    sa.B_u = B_u; sa.MD = MD;
+    sa.L = std::max(4, ceil_div(B_c, p->seg_T));     // ceil(B_c / L) <= seg_T chunks
+    sa.n_chunks = ceil_div(B_c, sa.L); sa.n_slices = p->seg_slices;
+    if ((e = launch_segsum(sa, s)) != hipSuccess) return hip_fail(e, "bwd segsum");
+
+    // dU[u] = [W_u^T | W_u^T] . [S_hi; S_lo] on the flat engine.
+    TileGemmArgs ua{};
+    ua.X = p->S2; ua.W = p->W_dup; ua.out = dU; ua.err = p->err; ua.map = map;
+    ua.B = B_u; ua.K = 2 * M; ua.M = K_u; ua.D = D; ua.ldw = p->du_ldw; ua.B_u = B_u;
+    ua.BD = (long long)B_u * D;
+    ua.n_ks = ceil_div(2 * M, 32); ua.n_ks_full = 2 * M / 32;
+    ua.n_mchunks = p->du_nmc;
+    if ((e = launch_tile_gemm(DT_BF16, EPI_STORE_T, p->du_tile, ua, s)) != hipSuccess) return hip_fail(e, "bwd dU");
+
+    // dW_u partials: sum over users of [S_hi; S_lo] . U[u]^T.
+    WgradArgs wu{};
+    wu.A = p->S2; wu.B = static_cast<const uint16_t *>(U); wu.part = p->part_u;
+    wu.E = B_u; wu.R = 2 * M; wu.N = K_u; wu.D = D;
+    wu.per_chunk = ceil_div(B_u, p->wgu_chunks);
+    wu.n_chunks = ceil_div(B_u, wu.per_chunk);
+    wu.n_rt = ceil_div(ceil_div(2 * M, 16), kWgradMR);
+    wu.n_nt = ceil_div(ceil_div(K_u, 16), kWgradNC);
+    wu.tgroups = ceil_div(wu.n_rt * wu.n_nt, 4);
+    if ((e = launch_wgrad(wu, s)) != hipSuccess) return hip_fail(e, "bwd dW_u");
+
+    WgradReduceArgs ra{};
+    ra.part_c = p->part_c; ra.part_u = p->part_u; ra.dW_c = dW_c; ra.dW_u = dW_u;
+    ra.P_c = P_c; ra.P_u = wu.n_chunks; ra.M = M; ra.K_u = K_u; ra.K_c = K_c;
+    if ((e = launch_wgrad_reduce(ra, s)) != hipSuccess) return hip_fail(e, "bwd reduce");
+    return IKBO_OK;
 }
 
 }  // extern "C"

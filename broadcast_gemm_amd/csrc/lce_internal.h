@@ -138,4 +138,56 @@ size_t rows_lds_bytes(const RowArgs &a);   // dynamic LDS of one launch (staged 
 int rows_blocks_per_cu(int epi, int D, int mb, size_t lds_bytes);
 hipError_t launch_rows(int epi, int mb, const RowArgs &a, int grid, hipStream_t s);
 
+// ---- backward (lce_backward.hip) -----------------------------------------------------------
+
+constexpr int kBwdPrepBlock = 1024;
+constexpr int kWgradMR = 3;   // 16-row blocks of A per wave tile
+constexpr int kWgradNC = 4;   // 16-row blocks of B per wave tile
+
+// Grouping of the candidates by user (block 0) and the transposed projections (the rest).
+struct BwdPrepArgs {
+    const int32_t *map;
+    int32_t *perm, *su, *off;     // [B_c], [B_c], [B_u + 1]
+    uint32_t *err;
+    const uint16_t *W_u, *W_c;    // [M][K_u], [M][K_c]
+    uint16_t *Wt_c;               // [K_c][M]
+    uint16_t *W_dup;              // [>= K_u][ldw_dup]: row k = W_u[:, k], W_u[:, k], zeros
+    int B_u, B_c, M, K_u, K_c, ldw_dup;
+};
+size_t bwd_prep_lds_bytes(int B_u, int B_c);
+hipError_t launch_bwd_prep(const BwdPrepArgs &a, hipStream_t s);
+
+// S[u] = sum of dY[b] over the candidates of user u, stored as S2[u] = [bf16(S); bf16(S - hi)].
+struct SegsumArgs {
+    const uint16_t *dY;           // [B_c][MD]
+    const int32_t *perm, *su, *off;
+    float *part;                  // [n_chunks + B_u - 1][MD] partial slots
+    uint16_t *S2;                 // [B_u][2][MD]
+    int B_u, MD;                  // MD = M*D (a multiple of 8)
+    int L;                        // sorted positions per chunk
+    int n_chunks;                 // ceil(B_c / L)
+    int n_slices;                 // ceil(MD / 512)
+};
+hipError_t launch_segsum(const SegsumArgs &a, hipStream_t s);
+
+// part[c][r][n] = sum over entries e of chunk c and d < D of A[e][r][d] * B[e][n][d].
+struct WgradArgs {
+    const uint16_t *A;            // [E][R][D]
+    const uint16_t *B;            // [E][N][D]
+    float *part;                  // [n_chunks][R][N]
+    int E, R, N, D;               // D a multiple of 32
+    int per_chunk, n_chunks;      // entries per chunk, ceil(E / per_chunk)
+    int n_rt, n_nt;               // tiles of 16*kWgradMR rows and 16*kWgradNC columns
+    int tgroups;                  // blocks per chunk: ceil(n_rt * n_nt / 4)
+};
+hipError_t launch_wgrad(const WgradArgs &a, hipStream_t s);
+
+struct WgradReduceArgs {
+    const float *part_c;          // [P_c][M][K_c]
+    const float *part_u;          // [P_u][2M][K_u]
+    float *dW_c, *dW_u;
+    int P_c, P_u, M, K_u, K_c;
+};
+hipError_t launch_wgrad_reduce(const WgradReduceArgs &a, hipStream_t s);
+
 }  // namespace ikbo

@@ -20,7 +20,11 @@ Draw recipe (a reading; the pages give no seeds or generator):
   * bf16 configurations round every drawn float32 to bfloat16 with
     round-to-nearest-even; the same bytes feed both the oracle and the GPU;
   * sorted maps give user ``i`` a contiguous run of candidates; when B_c is not
-    a multiple of B_u the first ``B_c mod B_u`` users get one extra candidate.
+    a multiple of B_u the first ``B_c mod B_u`` users get one extra candidate;
+  * the backward's upstream gradient dY [B_c, M, D] is drawn as float32 standard
+    normals from its own generator, seed = configuration seed + 1000, and stored
+    like the inputs (the pages describe no training setup; unit-scale gradients
+    are the plain reading).
 """
 from __future__ import annotations
 
@@ -162,6 +166,12 @@ def make_inputs(cfg: LceConfig, seed: Optional[int] = None) -> LceInputs:
     else:
         mp = sorted_map(cfg.B_u, cfg.B_c)
     return LceInputs(cfg, U, C, W_u, W_c, mp)
+
+
+def make_upstream_grad(cfg: LceConfig, seed: Optional[int] = None) -> np.ndarray:
+    """dY [B_c, M, D] for the backward, with the recipe in the module docstring."""
+    rng = np.random.default_rng(cfg.seed + 1000 if seed is None else seed)
+    return _store(rng.standard_normal((cfg.B_c, cfg.M, cfg.D), dtype=np.float32), cfg.dtype)
 
 
 def make_integer_inputs(cfg: LceConfig, seed: int = 12345) -> LceInputs:

@@ -1,6 +1,6 @@
 /*
- * ikbo.h -- C ABI of libikbo: the IKBO Linear Compression Embedding forward on
- * AMD Instinct MI355X (gfx950).
+ * ikbo.h -- C ABI of libikbo: the IKBO Linear Compression Embedding forward (and its
+ * backward) on AMD Instinct MI355X (gfx950).
  *
  * The operation (IKBO recsys blog, "Deep Dive: Linear Compression"; aibriefing
  * article, "kernel deep-dive case 1"):
@@ -78,7 +78,8 @@ enum {
 /* Plan flags (host-forced test conditions; production callers pass 0). */
 enum {
     IKBO_FLAG_DEBUG_DELAY_USER = 2, /* S4: user tiles sleep before computing (exercises the wait) */
-    IKBO_FLAG_DEBUG_SKIP_USER = 4   /* S4: user tiles publish nothing; candidates time out */
+    IKBO_FLAG_DEBUG_SKIP_USER = 4,  /* S4: user tiles publish nothing; candidates time out */
+    IKBO_FLAG_BACKWARD = 8          /* also allocate the workspace of ikbo_lce_backward */
 };
 
 /*
@@ -112,8 +113,40 @@ int ikbo_lce_forward(ikbo_lce_plan_t plan, const void *U, const void *C, const i
                      int B_u, int B_c, int K_u, int K_c, int M, int D, void *stream);
 
 /*
+ * Enqueue the gradients of L = <dY, Y> for the forward above (the chain rule of the
+ * pages' definition, blog "Deep Dive: Linear Compression", stage 1; the pages give no
+ * training formulas):
+ *
+ *     dC[b] = W_c^T . dY[b]                    dW_c = sum_b dY[b] . C[b]^T
+ *     dU[u] = W_u^T . S[u]                     dW_u = sum_b dY[b] . U[map[b]]^T
+ *     S[u]  = sum of dY[b] over the candidates b with map[b] = u
+ *
+ * The replicated user tensor is not built in this direction either: the user
+ * gradient is summed per user first and multiplied at batch B_u.  Requires a plan
+ * made with IKBO_FLAG_BACKWARD (bf16, D in {32, 64, 128, 160, 192}; otherwise the
+ * plan call returns IKBO_ERR_UNSUPPORTED); the variant does not matter.
+ * Layouts (device memory owned by the caller, dense row-major):
+ *     dY [B_c, M, D] bf16 (input)         U, C, map, W_u, W_c as for the forward
+ *     dU [B_u, K_u, D] bf16 (output)      dC [B_c, K_c, D] bf16 (output)
+ *     dW_u [M, K_u] float32 (output)      dW_c [M, K_c] float32 (output)
+ * Every output is overwritten, not accumulated into; users that no candidate maps to
+ * get dU = 0, and B_c = 0 gives dU = 0 and dW = 0 (dY, C, map and dC may then be NULL).
+ * Products accumulate in float32; S is kept in float32 and handed to the bf16 matrix
+ * cores as the pair bf16(S) + bf16(S - bf16(S)); dU and dC are rounded once to bf16.
+ * Every pointer except map must be 16-byte aligned (map: 4-byte).  Asynchronous, like
+ * the forward: map entries outside [0, B_u) are skipped and reported by ikbo_lce_check
+ * as IKBO_ERR_MAP_RANGE.  Uses the plan's workspace: do not overlap it with a forward
+ * or another backward on the same plan in a different stream.
+ * Errors (before anything is enqueued): INVALID_ARG, ALIGNMENT, UNSUPPORTED, HIP.
+ */
+int ikbo_lce_backward(ikbo_lce_plan_t plan, const void *dY, const void *U, const void *C,
+                      const int32_t *map, const void *W_u, const void *W_c, void *dU, void *dC,
+                      float *dW_u, float *dW_c, int B_u, int B_c, int K_u, int K_c, int M, int D,
+                      void *stream);
+
+/*
  * Wait for `stream`, then return and clear the device-side status recorded by
- * earlier forwards on this plan (IKBO_OK, IKBO_ERR_MAP_RANGE or
+ * earlier forwards and backwards on this plan (IKBO_OK, IKBO_ERR_MAP_RANGE or
  * IKBO_ERR_TIMEOUT), or IKBO_ERR_HIP if the wait itself failed.
  */
 int ikbo_lce_check(ikbo_lce_plan_t plan, void *stream);

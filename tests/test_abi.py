@@ -94,3 +94,13 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(bga, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         bga.lib()
+
+
+def test_backward_rejects_bad_arguments_before_hip(L):
+    h = ctypes.c_void_p()
+    # The backward's workspace exists for bf16 row-tile layouts only.
+    assert L.ikbo_lce_plan(ctypes.byref(h), 2, 8, 13, 11, 8, 16, 1, 0, bga.FLAG_BACKWARD) == bga.IKBO_ERR_UNSUPPORTED
+    assert L.ikbo_lce_plan(ctypes.byref(h), 2, 8, 13, 11, 8, 48, 0, 0, bga.FLAG_BACKWARD) == bga.IKBO_ERR_UNSUPPORTED
+    assert h.value is None
+    # No plan: rejected before any HIP call.
+    assert L.ikbo_lce_backward(None, *([None] * 10), 1, 1, 13, 11, 8, 16, None) == bga.IKBO_ERR_INVALID_ARG

@@ -122,9 +122,12 @@ MUTANTS = {
 
 def _build_mutant(tmp_path, name, old, new):
     src = open(ORACLE_SRC).read()
-    assert src.count(old) == 1, f"mutant {name}: anchor not found once in the oracle source"
+    # The forward's slips are planted in the forward function only (the backward follows it).
+    cut = src.index("int ikbo_oracle_lce_backward_f64(")
+    fwd, rest = src[:cut], src[cut:]
+    assert fwd.count(old) == 1, f"mutant {name}: anchor not found once in the oracle's forward"
     path = tmp_path / f"{name}.c"
-    path.write_text(src.replace(old, new))
+    path.write_text(fwd.replace(old, new) + rest)
     so = tmp_path / f"lib{name}.so"
     subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-std=c11",
                     "-o", str(so), str(path)], check=True)
