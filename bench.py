@@ -220,6 +220,141 @@ def run_rewrite(args, cfg, sets) -> int:
     return 0 if st == 0 else 1
 
 
+def backward_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one backward: dY, C, U, W_u, W_c and map read once; dC, dU
+    (input dtype) and dW_u, dW_c (fp32) written once."""
+    e = cfg.elt_size
+    return (e * (cfg.B_c * cfg.M * cfg.D + 2 * cfg.B_c * cfg.K_c * cfg.D + 2 * cfg.B_u * cfg.K_u * cfg.D
+                 + cfg.M * (cfg.K_u + cfg.K_c)) + 4 * cfg.M * (cfg.K_u + cfg.K_c) + 4 * cfg.B_c)
+
+
+def backward_flops(cfg) -> int:
+    """dC and dW_c per candidate, dU and dW_u per user (the decomposed form)."""
+    return 2 * cfg.M * cfg.D * (2 * cfg.B_c * cfg.K_c + 2 * cfg.B_u * cfg.K_u)
+
+
+def run_backward(args, cfg, x) -> int:
+    """Time the whole backward (every launch of ikbo_lce_backward) on rotating buffer sets."""
+    import numpy as np
+    import torch
+
+    import broadcast_gemm_amd as bga
+    from broadcast_gemm_amd.inputs import make_upstream_grad
+
+    dY0 = make_upstream_grad(cfg)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    base = [dev(a) for a in (dY0, x.U, x.C, x.map, x.W_u, x.W_c)]
+    tdt = base[0].dtype
+    outs0 = [torch.empty((cfg.B_u, cfg.K_u, cfg.D), dtype=tdt, device="cuda"),
+             torch.empty((cfg.B_c, cfg.K_c, cfg.D), dtype=tdt, device="cuda"),
+             torch.empty((cfg.M, cfg.K_u), dtype=torch.float32, device="cuda"),
+             torch.empty((cfg.M, cfg.K_c), dtype=torch.float32, device="cuda")]
+    set_bytes = sum(t.numel() * t.element_size() for t in base + outs0)
+    n_sets = max(1, math.ceil(args.rotate_mb * 2**20 / set_bytes))
+    sets = []
+    for i in range(n_sets):
+        ins = base if i == 0 else [t.clone() for t in base]
+        outs = outs0 if i == 0 else [torch.empty_like(t) for t in outs0]
+        sets.append(ins + outs)
+    plan = bga.LcePlan(cfg.B_u, cfg.B_c, cfg.K_u, cfg.K_c, cfg.M, cfg.D, dtype=cfg.dtype,
+                       flags=bga.FLAG_BACKWARD)
+    info = plan.info()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(i):
+        dY, U, C, mp, W_u, W_c, dU, dC, dW_u, dW_c = sets[i % n_sets]
+        st = plan.backward_ptrs(dY.data_ptr(), U.data_ptr(), C.data_ptr(), mp.data_ptr(), W_u.data_ptr(),
+                                W_c.data_ptr(), dU.data_ptr(), dC.data_ptr(), dW_u.data_ptr(), dW_c.data_ptr(),
+                                cfg.B_u, cfg.B_c, sh)
+        if st != bga.IKBO_OK:
+            raise bga.IkboError(st, "ikbo_lce_backward")
+
+    for i in range(args.warmup):
+        step(i)
+    st = plan.check()
+    if st != bga.IKBO_OK:
+        raise bga.IkboError(st, "warmup device status")
+    K = args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(K):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    st = plan.check()
+    if st != bga.IKBO_OK:
+        raise bga.IkboError(st, "timed device status")
+    ms = t0.elapsed_time(t1) / K
+
+    # Parity of set 0 against the oracle on sampled rows (untimed).
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from broadcast_gemm_amd.inputs import bf16_bits_to_f32
+
+        def host(t):
+            if t.dtype == torch.bfloat16:
+                return bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+            return t.cpu().numpy().astype(np.float64)
+        dU, dC, dW_u, dW_c = (host(t) for t in sets[0][6:])
+        bs = sorted(set([0, cfg.B_c // 2, cfg.B_c - 1]))
+        dc = [(b, k) for b in bs for k in (0, cfg.K_c - 1)]
+        du = [(int(x.map[0]), 0), (int(x.map[-1]), cfg.K_u - 1)]
+        dw = [(0, 0), (cfg.M - 1, cfg.K_u + cfg.K_c - 1), (cfg.M // 2, cfg.K_u)]
+        oc, ou, ow = oracle.lce_backward_rows_f64(dY0, x.U, x.C, x.map, x.W_u, x.W_c, dc, du, dw)
+        gw = np.array([dW_u[m, k] if k < cfg.K_u else dW_c[m, k - cfg.K_u] for m, k in dw])
+        nbad = sum(oracle.tolerance_violations(g, r)[0] for g, r in
+                   ((np.stack([dC[b, k] for b, k in dc]), oc), (np.stack([dU[u, k] for u, k in du]), ou), (gw, ow)))
+        parity = {"rows_checked": len(dc) + len(du) + len(dw), "violations": nbad}
+
+    nbytes, flops = backward_bytes(cfg), backward_flops(cfg)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "IKBO-LCE backward GB/s (algorithmic bytes) at B_c=1024, 70:1",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "B_u": cfg.B_u, "B_c": cfg.B_c, "K_u": cfg.K_u, "K_c": cfg.K_c,
+                   "M": cfg.M, "D": cfg.D, "map": cfg.map_kind, "rotating_sets": n_sets,
+                   "parallelism": "single GPU"},
+        "us_per_backward": round(ms * 1e3, 3),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+        "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole backward (every launch of one ikbo_lce_backward)"},
+        "plan": info, "parity": parity,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        # A bounded sample: the oracle's full backward on the first n candidates (and every
+        # user), repeated for about cpu_seconds; GB/s by the same byte count at that size.
+        n = max(1, min(cfg.B_c, 32))
+        sub = cfg.with_batch(cfg.B_u, n)
+        threads = oracle.max_threads()
+        reps, c0 = 0, time.perf_counter()
+        while True:
+            oracle.lce_backward_f64(dY0[:n], x.U, x.C[:n], x.map[:n], x.W_u, x.W_c, threads=threads)
+            reps += 1
+            el = time.perf_counter() - c0
+            if el >= args.cpu_seconds or reps >= 50:
+                break
+        out["cpu_baseline"] = {"value": round(backward_bytes(sub) * reps / el / 1e9, 4), "unit": "GB/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"first {n} candidates of {cfg.name} (all users), full backward x {reps}; "
+                                         f"{el:.1f} s wall"}
+    plan.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def run_copy(args) -> int:
     """Plain device copy of known size (calibrates FETCH_SIZE/WRITE_SIZE counters)."""
     import torch
@@ -243,7 +378,7 @@ def main() -> int:
     ap.add_argument("--rotate-mb", type=int, default=1100, help="total size of rotated buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--mode", default="lce", choices=["lce", "copy", "traffic", "rewrite"])
+    ap.add_argument("--mode", default="lce", choices=["lce", "copy", "traffic", "rewrite", "backward"])
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="--mode traffic: rocprofv3 --pmc output directories")
@@ -280,6 +415,8 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
+    if args.mode == "backward":
+        return run_backward(args, cfg, x)
     base = [dev(a) for a in (x.U, x.C, x.map, x.W_u, x.W_c)]
     tdt = base[0].dtype
     set_bytes = sum(t.numel() * t.element_size() for t in base) + cfg.B_c * cfg.M * cfg.D * base[0].element_size()

@@ -233,7 +233,7 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
         // summation order, and with it every bit of S, does not depend on the plan's capacity).
         p->seg_T = std::max(1, seg_waves / slices);
         p->wgc_chunks = std::max(1, std::min(env_int("IKBO_BWD_WGC_CHUNKS", 128), std::max(max_B_c, 1)));
-        p->wgu_chunks = std::max(1, std::min(8, max_B_u));
+        p->wgu_chunks = std::max(1, std::min(env_int("IKBO_BWD_WGU_CHUNKS", 64), max_B_u));
         if (p->dc_bpc < 1 || (long long)p->dc_mpad * D * 4 >= (1LL << 31) ||
             bwd_prep_lds_bytes(max_B_u, max_B_c) > (size_t)std::min(max_lds, 64 * 1024)) {
             delete p;
@@ -671,20 +671,6 @@ int ikbo_lce_backward(ikbo_lce_plan_t p, const void *dY, const void *U, const vo
         if ((e = launch_rows(EPI_STORE_T, p->dc_mb, c, grid, s)) != hipSuccess) return hip_fail(e, "bwd dC");
     }
 
-    // dW_c partials: sum over candidates of dY[b] . C[b]^T.
-    WgradArgs wc{};
-    int P_c = 0;
-    if (B_c > 0) {
-        wc.A = static_cast<const uint16_t *>(dY); wc.B = static_cast<const uint16_t *>(C); wc.part = p->part_c;
-        wc.E = B_c; wc.R = M; wc.N = K_c; wc.D = D;
-        wc.per_chunk = ceil_div(B_c, p->wgc_chunks);
-        wc.n_chunks = P_c = ceil_div(B_c, wc.per_chunk);
-        wc.n_rt = ceil_div(ceil_div(M, 16), kWgradMR);
-        wc.n_nt = ceil_div(ceil_div(K_c, 16), kWgradNC);
-        wc.tgroups = ceil_div(wc.n_rt * wc.n_nt, 4);
-        if ((e = launch_wgrad(wc, s)) != hipSuccess) return hip_fail(e, "bwd dW_c");
-    }
-
     // S[u] = sum of dY over the user's candidates, as [bf16(S); bf16(S - hi)].
     SegsumArgs sa{};
     sa.dY = static_cast<const uint16_t *>(dY); sa.perm = p->perm; sa.su = p->su; sa.off = p->off;
@@ -703,20 +689,22 @@ int ikbo_lce_backward(ikbo_lce_plan_t p, const void *dY, const void *U, const vo
     ua.n_mchunks = p->du_nmc;
     if ((e = launch_tile_gemm(DT_BF16, EPI_STORE_T, p->du_tile, ua, s)) != hipSuccess) return hip_fail(e, "bwd dU");
 
-    // dW_u partials: sum over users of [S_hi; S_lo] . U[u]^T.
-    WgradArgs wu{};
+    // Weight-gradient partials in one launch: sum over candidates of dY[b] . C[b]^T, and
+    // over users of [S_hi; S_lo] . U[u]^T.
+    WgradArgs wa{};
+    WgradProblem &wc = wa.p[0], &wu = wa.p[1];
+    wc.A = static_cast<const uint16_t *>(dY); wc.B = static_cast<const uint16_t *>(C); wc.part = p->part_c;
+    wc.E = B_c; wc.R = M; wc.N = K_c;
+    wgrad_problem_setup(wc, p->wgc_chunks);
     wu.A = p->S2; wu.B = static_cast<const uint16_t *>(U); wu.part = p->part_u;
-    wu.E = B_u; wu.R = 2 * M; wu.N = K_u; wu.D = D;
-    wu.per_chunk = ceil_div(B_u, p->wgu_chunks);
-    wu.n_chunks = ceil_div(B_u, wu.per_chunk);
-    wu.n_rt = ceil_div(ceil_div(2 * M, 16), kWgradMR);
-    wu.n_nt = ceil_div(ceil_div(K_u, 16), kWgradNC);
-    wu.tgroups = ceil_div(wu.n_rt * wu.n_nt, 4);
-    if ((e = launch_wgrad(wu, s)) != hipSuccess) return hip_fail(e, "bwd dW_u");
+    wu.E = B_u; wu.R = 2 * M; wu.N = K_u;
+    wgrad_problem_setup(wu, p->wgu_chunks);
+    wa.n_prob = 2; wa.D = D;
+    if ((e = launch_wgrad(wa, s)) != hipSuccess) return hip_fail(e, "bwd dW");
 
     WgradReduceArgs ra{};
     ra.part_c = p->part_c; ra.part_u = p->part_u; ra.dW_c = dW_c; ra.dW_u = dW_u;
-    ra.P_c = P_c; ra.P_u = wu.n_chunks; ra.M = M; ra.K_u = K_u; ra.K_c = K_c;
+    ra.P_c = wc.n_chunks; ra.P_u = wu.n_chunks; ra.M = M; ra.K_u = K_u; ra.K_c = K_c;
     if ((e = launch_wgrad_reduce(ra, s)) != hipSuccess) return hip_fail(e, "bwd reduce");
     return IKBO_OK;
 }

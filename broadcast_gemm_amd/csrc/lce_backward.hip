@@ -37,6 +37,8 @@ namespace ikbo {
 
 namespace {
 
+constexpr int kReduceRuns = 8;   // thread groups per output in the weight-gradient reduce
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -253,22 +255,25 @@ __global__ void __launch_bounds__(256) segsum_combine_kernel(SegsumArgs a) {
 // The four waves of a block take four tiles of one chunk, and the blocks of one chunk sit
 // on the same XCD (block index mod 8), so the chunk's rows are fetched into one L2.
 template <int MR, int NC, int NS>
-__global__ void __launch_bounds__(256) wgrad_kernel(WgradArgs a) {
+__global__ void __launch_bounds__(256) wgrad_kernel(WgradArgs args) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int g = lane >> 4, j = lane & 15;
-    const int xcd = (int)(blockIdx.x & 7u), slot = (int)(blockIdx.x >> 3);
+    const bool second = args.n_prob > 1 && (int)blockIdx.x >= args.p[0].blocks;
+    const WgradProblem a = second ? args.p[1] : args.p[0];   // a copy: fields stay in registers
+    const int bx = (int)blockIdx.x - (second ? args.p[0].blocks : 0);   // problem 0's count is a multiple of 8
+    const int xcd = bx & 7, slot = bx >> 3;
     const int chunk = (slot / a.tgroups) * 8 + xcd;
     const int tile = (slot % a.tgroups) * 4 + wv;
     if (chunk >= a.n_chunks || tile >= a.n_rt * a.n_nt) return;
     const int r0 = (tile % a.n_rt) * 16 * MR, n0 = (tile / a.n_rt) * 16 * NC;
     const int e0 = chunk * a.per_chunk;
     const int e1 = imin_t(e0 + a.per_chunk, a.E);
-    const int KS = a.D / 32;
-    const int n_steps = (int)__builtin_amdgcn_readfirstlane(e1 > e0 ? (e1 - e0) * KS : 0);
-    const int rowb = a.D * 2;                      // bytes per row
-    const int offA = (r0 + j) * rowb + 16 * g;     // lane's byte offset in block 0, step 0
-    const int offB = (n0 + j) * rowb + 16 * g;
-    const int A_bytes = a.R * rowb, B_bytes = a.N * rowb;
+    const int D = args.D;
+    const int KB = D * 2;                          // bytes per row = 64 bytes per 32-column step
+    const int n_steps = (int)__builtin_amdgcn_readfirstlane(e1 > e0 ? (e1 - e0) * (D / 32) : 0);
+    const int offA = (r0 + j) * KB + 16 * g;       // lane's byte offset in block 0, step 0
+    const int offB = (n0 + j) * KB + 16 * g;
+    const int A_bytes = a.R * KB, B_bytes = a.N * KB;
 
     f32x4_t acc[MR][NC];
 #pragma unroll
@@ -277,27 +282,32 @@ __global__ void __launch_bounds__(256) wgrad_kernel(WgradArgs a) {
         for (int nc = 0; nc < NC; ++nc) acc[mr][nc] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     u32x4_t ra[NS][MR], rb[NS][NC];
 
-    auto issue = [&](u32x4_t (&xa)[MR], u32x4_t (&xb)[NC], int s) {
-        const bool ok = s < n_steps;
-        const int e = e0 + (ok ? s / KS : 0);
-        const int kb = ok ? (s % KS) * 64 : 0;     // 32 columns of bf16
-        const __amdgpu_buffer_rsrc_t rsA = uniform_rsrc(ok ? a.A + (size_t)e * a.R * a.D : nullptr, ok ? A_bytes : 0);
-        const __amdgpu_buffer_rsrc_t rsB = uniform_rsrc(ok ? a.B + (size_t)e * a.N * a.D : nullptr, ok ? B_bytes : 0);
+    // The next step to issue: entry ie, byte offset ikb within its rows (wave-uniform).
+    int ie = e0, ikb = 0;
+    auto issue = [&](u32x4_t (&xa)[MR], u32x4_t (&xb)[NC]) {
+        const bool ok = ie < e1;
+        const __amdgpu_buffer_rsrc_t rsA = uniform_rsrc(ok ? a.A + (size_t)ie * a.R * D : nullptr, ok ? A_bytes : 0);
+        const __amdgpu_buffer_rsrc_t rsB = uniform_rsrc(ok ? a.B + (size_t)ie * a.N * D : nullptr, ok ? B_bytes : 0);
 #pragma unroll
         for (int mr = 0; mr < MR; ++mr)
             xa[mr] = __builtin_bit_cast(u32x4_t,
-                                        __builtin_amdgcn_raw_buffer_load_b128(rsA, offA + mr * 16 * rowb + kb, 0, 0));
+                                        __builtin_amdgcn_raw_buffer_load_b128(rsA, offA + mr * 16 * KB + ikb, 0, 0));
 #pragma unroll
         for (int nc = 0; nc < NC; ++nc)
             xb[nc] = __builtin_bit_cast(u32x4_t,
-                                        __builtin_amdgcn_raw_buffer_load_b128(rsB, offB + nc * 16 * rowb + kb, 0, 0));
+                                        __builtin_amdgcn_raw_buffer_load_b128(rsB, offB + nc * 16 * KB + ikb, 0, 0));
+        ikb += 64;
+        if (ikb == KB) {
+            ikb = 0;
+            ++ie;
+        }
     };
 #pragma unroll
-    for (int q = 0; q < NS - 1; ++q) issue(ra[q], rb[q], q);
+    for (int q = 0; q < NS - 1; ++q) issue(ra[q], rb[q]);
     for (int s = 0; s < n_steps; s += NS) {
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
-            issue(ra[(q + NS - 1) % NS], rb[(q + NS - 1) % NS], s + q + NS - 1);
+            issue(ra[(q + NS - 1) % NS], rb[(q + NS - 1) % NS]);
 #pragma unroll
             for (int mr = 0; mr < MR; ++mr)
 #pragma unroll
@@ -319,25 +329,50 @@ __global__ void __launch_bounds__(256) wgrad_kernel(WgradArgs a) {
 }
 
 // dW_c[m][k] = sum over chunks of part_c; dW_u[m][k] = sum over chunks of the hi row m and
-// the lo row M + m of part_u.  Chunks are added in order.
+// the lo row M + m of part_u.  A block takes 32 outputs; its 8 thread groups each add a run
+// of consecutive chunks (their loads all in flight), and the 8 run sums are then added in
+// run order, so the result does not depend on the launch.
 __global__ void __launch_bounds__(256) wgrad_reduce_kernel(WgradReduceArgs a) {
+    __shared__ float part[kReduceRuns][32];
+    const int o = (int)(threadIdx.x & 31), run = (int)(threadIdx.x >> 5);
     const long long n_c = (long long)a.M * a.K_c, n_u = (long long)a.M * a.K_u;
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n_c + n_u;
-         i += (long long)gridDim.x * blockDim.x) {
-        if (i < n_c) {
-            float s = 0.0f;
-            for (int c = 0; c < a.P_c; ++c) s += a.part_c[(size_t)c * n_c + i];
-            a.dW_c[i] = s;
-        } else {
-            const long long t = i - n_c;
-            float s = 0.0f;
-            for (int c = 0; c < a.P_u; ++c) {
-                const float *p = a.part_u + (size_t)c * 2 * n_u;
-                s += p[t];
-                s += p[n_u + t];
+    const long long i = (long long)blockIdx.x * 32 + o;
+    const bool is_c = i < n_c;
+    const int P = is_c ? a.P_c : a.P_u;
+    const int per = (P + kReduceRuns - 1) / kReduceRuns;
+    const int c0 = run * per, c1 = imin_t(c0 + per, P);
+    float s = 0.0f;
+    if (i < n_c + n_u) {
+        constexpr int QB = 16;
+        for (int c = c0; c < c1; c += QB) {
+            float v[QB], w[QB];
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                const bool ok = c + q < c1;
+                if (is_c) {
+                    v[q] = ok ? a.part_c[(size_t)(c + q) * n_c + i] : 0.0f;
+                    w[q] = 0.0f;
+                } else {
+                    const float *p = a.part_u + (size_t)(c + q) * 2 * n_u + (i - n_c);
+                    v[q] = ok ? p[0] : 0.0f;
+                    w[q] = ok ? p[n_u] : 0.0f;
+                }
             }
-            a.dW_u[t] = s;
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                s += v[q];
+                s += w[q];
+            }
         }
+    }
+    part[run][o] = s;
+    __syncthreads();
+    if (run == 0 && i < n_c + n_u) {
+        float t = part[0][o];
+#pragma unroll
+        for (int r = 1; r < kReduceRuns; ++r) t += part[r][o];
+        if (is_c) a.dW_c[i] = t;
+        else a.dW_u[i - n_c] = t;
     }
 }
 
@@ -371,16 +406,31 @@ hipError_t launch_segsum(const SegsumArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+void wgrad_problem_setup(WgradProblem &p, int chunks_max) {
+    if (p.E <= 0) {
+        p.per_chunk = p.n_chunks = p.tgroups = p.blocks = 0;
+        p.n_rt = p.n_nt = 1;
+        return;
+    }
+    p.per_chunk = (p.E + chunks_max - 1) / chunks_max;
+    p.n_chunks = (p.E + p.per_chunk - 1) / p.per_chunk;
+    p.n_rt = ((p.R + 15) / 16 + kWgradMR - 1) / kWgradMR;
+    p.n_nt = ((p.N + 15) / 16 + kWgradNC - 1) / kWgradNC;
+    p.tgroups = (p.n_rt * p.n_nt + 3) / 4;
+    p.blocks = 8 * p.tgroups * ((p.n_chunks + 7) / 8);
+}
+
 hipError_t launch_wgrad(const WgradArgs &a, hipStream_t s) {
-    if (a.n_chunks == 0) return hipSuccess;
-    const unsigned grid = 8u * (unsigned)a.tgroups * (unsigned)((a.n_chunks + 7) / 8);
-    hipLaunchKernelGGL((wgrad_kernel<kWgradMR, kWgradNC, 4>), dim3(grid), dim3(256), 0, s, a);
+    const long long grid = (long long)a.p[0].blocks + (a.n_prob > 1 ? a.p[1].blocks : 0);
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((wgrad_kernel<kWgradMR, kWgradNC, kWgradNS>), dim3((unsigned)grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_wgrad_reduce(const WgradReduceArgs &a, hipStream_t s) {
     const long long n = (long long)a.M * (a.K_u + a.K_c);
-    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, a);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + 31) / 32)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

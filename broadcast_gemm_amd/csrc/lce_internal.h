@@ -143,6 +143,10 @@ hipError_t launch_rows(int epi, int mb, const RowArgs &a, int grid, hipStream_t 
 constexpr int kBwdPrepBlock = 1024;
 constexpr int kWgradMR = 3;   // 16-row blocks of A per wave tile
 constexpr int kWgradNC = 4;   // 16-row blocks of B per wave tile
+#ifndef IKBO_WGRAD_NS
+#define IKBO_WGRAD_NS 4
+#endif
+constexpr int kWgradNS = IKBO_WGRAD_NS;   // K steps in the register ring
 
 // Grouping of the candidates by user (block 0) and the transposed projections (the rest).
 struct BwdPrepArgs {
@@ -171,15 +175,23 @@ struct SegsumArgs {
 hipError_t launch_segsum(const SegsumArgs &a, hipStream_t s);
 
 // part[c][r][n] = sum over entries e of chunk c and d < D of A[e][r][d] * B[e][n][d].
-struct WgradArgs {
+struct WgradProblem {
     const uint16_t *A;            // [E][R][D]
     const uint16_t *B;            // [E][N][D]
     float *part;                  // [n_chunks][R][N]
-    int E, R, N, D;               // D a multiple of 32
+    int E, R, N;
     int per_chunk, n_chunks;      // entries per chunk, ceil(E / per_chunk)
     int n_rt, n_nt;               // tiles of 16*kWgradMR rows and 16*kWgradNC columns
     int tgroups;                  // blocks per chunk: ceil(n_rt * n_nt / 4)
+    int blocks;                   // 8 * tgroups * ceil(n_chunks / 8) (0: no work)
 };
+// Up to two problems in one launch: the blocks of problem 0, then those of problem 1.
+struct WgradArgs {
+    WgradProblem p[2];
+    int n_prob;
+    int D;                        // a multiple of 32
+};
+void wgrad_problem_setup(WgradProblem &p, int chunks_max);
 hipError_t launch_wgrad(const WgradArgs &a, hipStream_t s);
 
 struct WgradReduceArgs {
