@@ -246,15 +246,19 @@ __global__ void __launch_bounds__(256) segsum_combine_kernel(SegsumArgs a) {
 // ---- weight gradients -------------------------------------------------------------------------
 
 // One wave per (output tile of 16*MR rows x 16*NC columns, chunk of entries).  For each
-// entry and 32-column step of d, lane (g, j) loads row j of each 16-row block of A and of
-// B at columns 8g .. 8g+7 (one 16-byte load each) and feeds them to
+// entry, lane (g, j) loads row j of each 16-row block of A and of B at columns 32t + 8g ..
+// 32t + 8g + 7 for every 32-column step t (one 16-byte load each) and feeds them to
 // v_mfma_f32_16x16x32_bf16 as they are: out[r0 + 16*mr + 4g + i][n0 + 16*nc + j] += ...
-// Steps stream through a ring of NS register slots.  Each entry is read through buffer
-// resources that cover exactly its [R][D] and [N][D] matrices, so rows past R or N read as
-// zero; steps past the chunk's end use an empty resource (zeros, no memory traffic).
-// The four waves of a block take four tiles of one chunk, and the blocks of one chunk sit
-// on the same XCD (block index mod 8), so the chunk's rows are fetched into one L2.
-template <int MR, int NC, int NS>
+// The loads of a block are issued for all KS steps back to back, so a wave sweeps each
+// 16-row block as one contiguous span of memory (reading it column step by column step
+// across many rows instead runs at half the rate).  Entries are double-buffered in
+// registers: the next entry's loads are in flight while the current one is multiplied.
+// Each entry is read through buffer resources that cover exactly its [R][D] and [N][D]
+// matrices, so rows past R or N read as zero; an entry past the chunk's end uses an empty
+// resource (zeros, no memory traffic).  The four waves of a block take four tiles of one
+// chunk, and the blocks of one chunk sit on the same XCD (block index mod 8), so the
+// chunk's rows are fetched into one L2.
+template <int MR, int NC, int KS>
 __global__ void __launch_bounds__(256) wgrad_kernel(WgradArgs args) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int g = lane >> 4, j = lane & 15;
@@ -268,51 +272,51 @@ __global__ void __launch_bounds__(256) wgrad_kernel(WgradArgs args) {
     const int r0 = (tile % a.n_rt) * 16 * MR, n0 = (tile / a.n_rt) * 16 * NC;
     const int e0 = chunk * a.per_chunk;
     const int e1 = imin_t(e0 + a.per_chunk, a.E);
-    const int D = args.D;
-    const int KB = D * 2;                          // bytes per row = 64 bytes per 32-column step
-    const int n_steps = (int)__builtin_amdgcn_readfirstlane(e1 > e0 ? (e1 - e0) * (D / 32) : 0);
-    const int offA = (r0 + j) * KB + 16 * g;       // lane's byte offset in block 0, step 0
-    const int offB = (n0 + j) * KB + 16 * g;
-    const int A_bytes = a.R * KB, B_bytes = a.N * KB;
+    constexpr int D = 32 * KS;
+    constexpr int RB = 2 * D;                      // bytes per row
+    const int offA = (r0 + j) * RB + 16 * g;       // lane's byte offset in block 0, step 0
+    const int offB = (n0 + j) * RB + 16 * g;
+    const int A_bytes = a.R * RB, B_bytes = a.N * RB;
 
     f32x4_t acc[MR][NC];
 #pragma unroll
     for (int mr = 0; mr < MR; ++mr)
 #pragma unroll
         for (int nc = 0; nc < NC; ++nc) acc[mr][nc] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    u32x4_t ra[NS][MR], rb[NS][NC];
+    u32x4_t ra[2][MR][KS], rb[2][NC][KS];
 
-    // The next step to issue: entry ie, byte offset ikb within its rows (wave-uniform).
-    int ie = e0, ikb = 0;
-    auto issue = [&](u32x4_t (&xa)[MR], u32x4_t (&xb)[NC]) {
-        const bool ok = ie < e1;
-        const __amdgpu_buffer_rsrc_t rsA = uniform_rsrc(ok ? a.A + (size_t)ie * a.R * D : nullptr, ok ? A_bytes : 0);
-        const __amdgpu_buffer_rsrc_t rsB = uniform_rsrc(ok ? a.B + (size_t)ie * a.N * D : nullptr, ok ? B_bytes : 0);
+    auto issue = [&](u32x4_t (&xa)[MR][KS], u32x4_t (&xb)[NC][KS], int e) {
+        const bool ok = e < e1;
+        const __amdgpu_buffer_rsrc_t rsA = uniform_rsrc(ok ? a.A + (size_t)e * a.R * D : nullptr, ok ? A_bytes : 0);
+        const __amdgpu_buffer_rsrc_t rsB = uniform_rsrc(ok ? a.B + (size_t)e * a.N * D : nullptr, ok ? B_bytes : 0);
 #pragma unroll
         for (int mr = 0; mr < MR; ++mr)
-            xa[mr] = __builtin_bit_cast(u32x4_t,
-                                        __builtin_amdgcn_raw_buffer_load_b128(rsA, offA + mr * 16 * KB + ikb, 0, 0));
+#pragma unroll
+            for (int t = 0; t < KS; ++t)
+                xa[mr][t] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsA, offA + mr * 16 * RB + 64 * t, 0, 0));
 #pragma unroll
         for (int nc = 0; nc < NC; ++nc)
-            xb[nc] = __builtin_bit_cast(u32x4_t,
-                                        __builtin_amdgcn_raw_buffer_load_b128(rsB, offB + nc * 16 * KB + ikb, 0, 0));
-        ikb += 64;
-        if (ikb == KB) {
-            ikb = 0;
-            ++ie;
-        }
+#pragma unroll
+            for (int t = 0; t < KS; ++t)
+                xb[nc][t] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsB, offB + nc * 16 * RB + 64 * t, 0, 0));
     };
+    auto compute = [&](const u32x4_t (&xa)[MR][KS], const u32x4_t (&xb)[NC][KS]) {
 #pragma unroll
-    for (int q = 0; q < NS - 1; ++q) issue(ra[q], rb[q]);
-    for (int s = 0; s < n_steps; s += NS) {
+        for (int nc = 0; nc < NC; ++nc)
 #pragma unroll
-        for (int q = 0; q < NS; ++q) {
-            issue(ra[(q + NS - 1) % NS], rb[(q + NS - 1) % NS]);
+            for (int t = 0; t < KS; ++t)
 #pragma unroll
-            for (int mr = 0; mr < MR; ++mr)
-#pragma unroll
-                for (int nc = 0; nc < NC; ++nc) acc[mr][nc] = mfma_bf16(ra[q][mr], rb[q][nc], acc[mr][nc]);
-        }
+                for (int mr = 0; mr < MR; ++mr) acc[mr][nc] = mfma_bf16(xa[mr][t], xb[nc][t], acc[mr][nc]);
+    };
+    issue(ra[0], rb[0], e0);
+    for (int e = e0; e < e1; e += 2) {
+        issue(ra[1], rb[1], e + 1);
+        compute(ra[0], rb[0]);
+        if (e + 1 >= e1) break;
+        issue(ra[0], rb[0], e + 2);
+        compute(ra[1], rb[1]);
     }
     float *out = a.part + (size_t)chunk * a.R * a.N;
 #pragma unroll
@@ -423,7 +427,15 @@ void wgrad_problem_setup(WgradProblem &p, int chunks_max) {
 hipError_t launch_wgrad(const WgradArgs &a, hipStream_t s) {
     const long long grid = (long long)a.p[0].blocks + (a.n_prob > 1 ? a.p[1].blocks : 0);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((wgrad_kernel<kWgradMR, kWgradNC, kWgradNS>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    const dim3 g((unsigned)grid), b(256);
+    switch (a.D) {
+        case 32: hipLaunchKernelGGL((wgrad_kernel<kWgradMR, kWgradNC, 1>), g, b, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((wgrad_kernel<kWgradMR, kWgradNC, 2>), g, b, 0, s, a); break;
+        case 128: hipLaunchKernelGGL((wgrad_kernel<kWgradMR, kWgradNC, 4>), g, b, 0, s, a); break;
+        case 160: hipLaunchKernelGGL((wgrad_kernel<kWgradMR, kWgradNC, 5>), g, b, 0, s, a); break;
+        case 192: hipLaunchKernelGGL((wgrad_kernel<kWgradMR, kWgradNC, 6>), g, b, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

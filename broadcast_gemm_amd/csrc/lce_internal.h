@@ -143,10 +143,6 @@ hipError_t launch_rows(int epi, int mb, const RowArgs &a, int grid, hipStream_t 
 constexpr int kBwdPrepBlock = 1024;
 constexpr int kWgradMR = 3;   // 16-row blocks of A per wave tile
 constexpr int kWgradNC = 4;   // 16-row blocks of B per wave tile
-#ifndef IKBO_WGRAD_NS
-#define IKBO_WGRAD_NS 4
-#endif
-constexpr int kWgradNS = IKBO_WGRAD_NS;   // K steps in the register ring
 
 // Grouping of the candidates by user (block 0) and the transposed projections (the rest).
 struct BwdPrepArgs {
@@ -189,7 +185,7 @@ struct WgradProblem {
 struct WgradArgs {
     WgradProblem p[2];
     int n_prob;
-    int D;                        // a multiple of 32
+    int D;                        // 32, 64, 128, 160 or 192
 };
 void wgrad_problem_setup(WgradProblem &p, int chunks_max);
 hipError_t launch_wgrad(const WgradArgs &a, hipStream_t s);
