@@ -336,7 +336,7 @@ def run_backward(args, cfg, x) -> int:
         import oracle
         # A bounded sample: the oracle's full backward on the first n candidates (and every
         # user), repeated for about cpu_seconds; GB/s by the same byte count at that size.
-        n = max(1, min(cfg.B_c, 32))
+        n = max(1, min(cfg.B_c, 64))
         sub = cfg.with_batch(cfg.B_u, n)
         threads = oracle.max_threads()
         reps, c0 = 0, time.perf_counter()
@@ -344,7 +344,7 @@ def run_backward(args, cfg, x) -> int:
             oracle.lce_backward_f64(dY0[:n], x.U, x.C[:n], x.map[:n], x.W_u, x.W_c, threads=threads)
             reps += 1
             el = time.perf_counter() - c0
-            if el >= args.cpu_seconds or reps >= 50:
+            if el >= args.cpu_seconds or reps >= 1000:
                 break
         out["cpu_baseline"] = {"value": round(backward_bytes(sub) * reps / el / 1e9, 4), "unit": "GB/s",
                                "cores": threads, "kind": "oracle",

@@ -228,7 +228,7 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
         p->du_ldw = ceil_div(2 * M, 32) * 32;
         const int slices = ceil_div(M * D, 512);
         p->seg_slices = slices;
-        const int seg_waves = std::max(64, env_int("IKBO_BWD_SEG_WAVES", 2048));
+        const int seg_waves = std::max(64, env_int("IKBO_BWD_SEG_WAVES", 4096));
         // Chunks of the sorted candidate list: at most seg_T, sized from the call's B_c (so the
         // summation order, and with it every bit of S, does not depend on the plan's capacity).
         p->seg_T = std::max(1, seg_waves / slices);

@@ -114,8 +114,9 @@ int ikbo_lce_forward(ikbo_lce_plan_t plan, const void *U, const void *C, const i
 
 /*
  * Enqueue the gradients of L = <dY, Y> for the forward above (the chain rule of the
- * pages' definition, blog "Deep Dive: Linear Compression", stage 1; the pages give no
- * training formulas):
+ * pages' definition, blog "Deep Dive: Linear Compression", stage 1; the aibriefing
+ * article's three-layers paragraph says the kernels serve training when the ratio
+ * exceeds 1, but the pages give no training formulas):
  *
  *     dC[b] = W_c^T . dY[b]                    dW_c = sum_b dY[b] . C[b]^T
  *     dU[u] = W_u^T . S[u]                     dW_u = sum_b dY[b] . U[map[b]]^T
