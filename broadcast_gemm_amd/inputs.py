@@ -208,3 +208,63 @@ def make_tag_inputs(cfg: LceConfig, mp: Optional[np.ndarray] = None) -> LceInput
         mp = default_map(cfg)
     return LceInputs(cfg, _store(U, cfg.dtype), _store(C, cfg.dtype), _store(W_u, cfg.dtype),
                      _store(W_c, cfg.dtype), np.asarray(mp, dtype=np.int32))
+
+
+# ---- IKBO target attention ----------------------------------------------------------------
+#
+# Shape reading (the pages print no shapes for attention): standard attention over a
+# broadcast K/V is said to run at about 60 FLOP/B and the IKBO form at about 833 FLOP/B at
+# 70:1, with a user sequence of 1024 (IKBO recsys blog, "Deep Dive: Flash Attention").
+# With L_kv = 1024 both figures give L_q = 64 query tokens per candidate
+# (L_q L_kv / (L_kv + L_q) = 60.2 and L_q L_kv / (L_kv / 70 + L_q) = 833.5), and the quoted
+# 621 TFLOP/s at 0.230 ms for 1024 candidates gives H * head_dim of about 512: H = 4 heads
+# of 128.  Q, K, V are standard normals rounded to bf16 (scores then have unit variance).
+
+@dataclasses.dataclass(frozen=True)
+class FaConfig:
+    name: str
+    B_u: int
+    B_c: int
+    H: int
+    L_q: int
+    L_kv: int
+    hd: int
+    dtype: str
+    map_kind: str        # "sorted" or "random"
+    seed: int
+
+    @property
+    def elt_size(self) -> int:
+        return 2 if self.dtype == DTYPE_BF16 else 4
+
+
+FA_CONFIGS = [
+    FaConfig("fa-tiny", 2, 6, 2, 16, 40, 64, DTYPE_BF16, "sorted", 20),
+    FaConfig("fa-70to1", 15, 1024, 4, 64, 1024, 128, DTYPE_BF16, "sorted", 21),
+    FaConfig("fa-10to1", 26, 256, 4, 64, 1024, 128, DTYPE_BF16, "sorted", 22),
+    FaConfig("fa-large-unsorted", 59, 4096, 4, 64, 1024, 128, DTYPE_BF16, "random", 23),
+]
+FA_CONFIG_BY_NAME = {c.name: c for c in FA_CONFIGS}
+
+
+@dataclasses.dataclass
+class FaInputs:
+    cfg: FaConfig
+    Q: np.ndarray      # [B_c, H, L_q, hd]
+    K: np.ndarray      # [B_u, H, L_kv, hd]
+    V: np.ndarray      # [B_u, H, L_kv, hd]
+    map: np.ndarray    # [B_c] int32
+
+
+def make_fa_inputs(cfg: FaConfig, seed: Optional[int] = None) -> FaInputs:
+    """Draw Q, K, V (in that order) as float32 standard normals, then the map."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    Q = _store(rng.standard_normal((cfg.B_c, cfg.H, cfg.L_q, cfg.hd), dtype=np.float32), cfg.dtype)
+    K = _store(rng.standard_normal((cfg.B_u, cfg.H, cfg.L_kv, cfg.hd), dtype=np.float32), cfg.dtype)
+    V = _store(rng.standard_normal((cfg.B_u, cfg.H, cfg.L_kv, cfg.hd), dtype=np.float32), cfg.dtype)
+    if cfg.map_kind == "random":
+        mp = rng.integers(0, cfg.B_u, cfg.B_c).astype(np.int32)
+    else:
+        mp = sorted_map(cfg.B_u, cfg.B_c)
+    return FaInputs(cfg, Q, K, V, mp)
+

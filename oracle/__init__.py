@@ -1,4 +1,5 @@
-"""CPU oracle for the IKBO Linear Compression Embedding forward and its backward.
+"""CPU oracle for the IKBO Linear Compression Embedding forward and its backward, and for
+IKBO target attention.
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg are the only callers.  The product package never imports this
@@ -34,7 +35,7 @@ ORACLE_F32 = 1
 def build(verbose: bool = False) -> str:
     """Compile the oracle with gcc (always recompiles)."""
     cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
-           "-std=c11", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC]
+           "-std=c11", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -59,6 +60,9 @@ def _load():
         lib.ikbo_oracle_lce_backward_f64.restype = ctypes.c_int
         lib.ikbo_oracle_lce_backward_f64.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 6 + [
             ctypes.c_int] + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p] * 3 + [ctypes.c_int]
+        lib.ikbo_oracle_fa_f64.restype = ctypes.c_int
+        lib.ikbo_oracle_fa_f64.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 6 + [
+            ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int]
         lib.ikbo_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -176,6 +180,39 @@ def lce_backward_f64(dY: np.ndarray, U: np.ndarray, C: np.ndarray, mp: np.ndarra
     dW = ow.reshape(M, K_u + K_c)
     return (ou.reshape(B_u, K_u, D), oc.reshape(B_c, K_c, D), np.ascontiguousarray(dW[:, :K_u]),
             np.ascontiguousarray(dW[:, K_u:]))
+
+
+def fa_f64(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mp: np.ndarray, rows=None,
+           scale: Optional[float] = None, threads: int = 0) -> np.ndarray:
+    """IKBO target attention in fp64: O[b,h,q] = softmax(scale * Q[b,h,q] . K[map[b],h]^T) V[map[b],h].
+
+    Q [B_c, H, L_q, hd]; K, V [B_u, H, L_kv, hd]; all ``uint16`` bf16 bit patterns or all
+    ``float32``.  ``scale`` defaults to 1/sqrt(hd).  ``rows``: (b, h, q) triples (default:
+    every row); the result is [n, hd] for a list, else [B_c, H, L_q, hd]."""
+    dt = Q.dtype
+    if not all(a.dtype == dt for a in (K, V)):
+        raise TypeError("Q, K, V must share one dtype")
+    code = ORACLE_BF16 if dt == np.uint16 else ORACLE_F32 if dt == np.float32 else None
+    if code is None:
+        raise TypeError(f"unsupported dtype {dt}")
+    B_c, H, L_q, hd = Q.shape
+    B_u, H2, L_kv, hd2 = K.shape
+    if K.shape != V.shape or (H, hd) != (H2, hd2) or mp.shape != (B_c,):
+        raise ValueError("inconsistent shapes")
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(hd))
+    Q, K, V = (np.ascontiguousarray(a) for a in (Q, K, V))
+    mp = np.ascontiguousarray(mp, dtype=np.int32)
+    full = rows is None
+    if full:
+        rows = np.stack(np.meshgrid(np.arange(B_c), np.arange(H), np.arange(L_q), indexing="ij"), -1).reshape(-1, 3)
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+    O = np.empty((len(r), hd))
+    st = _load().ikbo_oracle_fa_f64(Q.ctypes.data, K.ctypes.data, V.ctypes.data, mp.ctypes.data, B_u, B_c, H, L_q,
+                                    L_kv, hd, float(scale), code, r.ctypes.data, len(r), O.ctypes.data, int(threads))
+    if st != 0:
+        raise OracleError(f"oracle returned {st}")
+    return O.reshape(B_c, H, L_q, hd) if full else O
 
 
 def tolerance_violations(Y_gpu: np.ndarray, Y_ref: np.ndarray, atol: float = 1e-3,

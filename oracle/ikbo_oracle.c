@@ -30,6 +30,7 @@
  *   U   [B_u, K_u, D]     C [B_c, K_c, D]     W_u [M, K_u]     W_c [M, K_c]
  *   map [B_c] int32, 0 <= map[b] < B_u        Y   [n_rows, M, D] double
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -241,6 +242,86 @@ int ikbo_oracle_lce_backward_f64(const void *dY, const void *U, const void *C, c
         dW[i] = acc;
     }
     free(W);
+    return status;
+}
+
+/*
+ * IKBO target attention (IKBO recsys blog, "Deep Dive: Flash Attention"): the queries of
+ * candidate b attend over the keys and values of its user u = map[b], head by head:
+ *
+ *     K_b = K[map[b]], V_b = V[map[b]]           (the broadcast, materialised here)
+ *     s_k = scale * sum_d Q[b,h,q,d] K_b[h,k,d]
+ *     O[b,h,q,:] = sum_k softmax(s)_k V_b[h,k,:]
+ *
+ * Layouts: Q, O [B_c][H][L_q][hd]; K, V [B_u][H][L_kv][hd].  Requested output rows are
+ * (b, h, q) triples; each gives hd values.  Per row: the materialised K_b and V_b rows of
+ * head h are copied into a buffer, scores summed over d ascending, the maximum score
+ * subtracted before exp (the value is the same; it only keeps exp finite), the weights and
+ * the weighted sum of V taken over k ascending, then divided by the sum of weights.
+ */
+int ikbo_oracle_fa_f64(const void *Q, const void *K, const void *V, const int32_t *map, int64_t B_u,
+                       int64_t B_c, int64_t H, int64_t L_q, int64_t L_kv, int64_t hd, double scale,
+                       int dtype, const int64_t *rows, int64_t n_rows, double *O, int nthreads)
+{
+    if (!Q || !K || !V || !map || !O || (n_rows && !rows)) return ORACLE_ERR_ARG;
+    if (B_u < 1 || B_c < 0 || H < 1 || L_q < 1 || L_kv < 1 || hd < 1) return ORACLE_ERR_ARG;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F32) return ORACLE_ERR_ARG;
+    for (int64_t b = 0; b < B_c; ++b)
+        if (map[b] < 0 || map[b] >= B_u) return ORACLE_ERR_MAP;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[3 * i] < 0 || rows[3 * i] >= B_c || rows[3 * i + 1] < 0 || rows[3 * i + 1] >= H ||
+            rows[3 * i + 2] < 0 || rows[3 * i + 2] >= L_q)
+            return ORACLE_ERR_ARG;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int status = ORACLE_OK;
+#pragma omp parallel
+    {
+        double *Kb = (double *)malloc(sizeof(double) * (size_t)(L_kv * hd));
+        double *Vb = (double *)malloc(sizeof(double) * (size_t)(L_kv * hd));
+        double *sc = (double *)malloc(sizeof(double) * (size_t)L_kv);
+        double *qv = (double *)malloc(sizeof(double) * (size_t)hd);
+        if (!Kb || !Vb || !sc || !qv) {
+#pragma omp atomic write
+            status = ORACLE_ERR_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t i = 0; i < n_rows; ++i) {
+                const int64_t b = rows[3 * i], h = rows[3 * i + 1], q = rows[3 * i + 2];
+                const int64_t u = map[b];
+                for (int64_t k = 0; k < L_kv; ++k)
+                    for (int64_t d = 0; d < hd; ++d) {
+                        Kb[k * hd + d] = widen(K, ((u * H + h) * L_kv + k) * hd + d, dtype);
+                        Vb[k * hd + d] = widen(V, ((u * H + h) * L_kv + k) * hd + d, dtype);
+                    }
+                for (int64_t d = 0; d < hd; ++d) qv[d] = widen(Q, ((b * H + h) * L_q + q) * hd + d, dtype);
+                double mx = -INFINITY;
+                for (int64_t k = 0; k < L_kv; ++k) {
+                    double t = 0.0;
+                    for (int64_t d = 0; d < hd; ++d) t += qv[d] * Kb[k * hd + d];
+                    sc[k] = scale * t;
+                    if (sc[k] > mx) mx = sc[k];
+                }
+                double l = 0.0;
+                for (int64_t k = 0; k < L_kv; ++k) {
+                    sc[k] = exp(sc[k] - mx);
+                    l += sc[k];
+                }
+                double *out = O + i * hd;
+                for (int64_t d = 0; d < hd; ++d) out[d] = 0.0;
+                for (int64_t k = 0; k < L_kv; ++k)
+                    for (int64_t d = 0; d < hd; ++d) out[d] += sc[k] * Vb[k * hd + d];
+                for (int64_t d = 0; d < hd; ++d) out[d] /= l;
+            }
+        }
+        free(Kb);
+        free(Vb);
+        free(sc);
+        free(qv);
+    }
     return status;
 }
 
