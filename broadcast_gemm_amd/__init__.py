@@ -12,6 +12,9 @@ if the library is not built, every call raises.
 
     plan = LcePlan(..., flags=FLAG_BACKWARD)     # the backward's workspace as well
     dU, dC, dW_u, dW_c = plan.backward(dY, U, C, map, W_u, W_c)
+
+    fa = FaPlan(max_B_u, max_B_c, H, L_q, L_kv, head_dim)   # IKBO target attention
+    O = fa.forward(Q, K, V, map)
 """
 from __future__ import annotations
 
@@ -38,7 +41,8 @@ FLAG_DEBUG_SKIP_USER = 4
 FLAG_BACKWARD = 8
 
 # Every symbol include/ikbo.h declares.
-EXPORTED = ("ikbo_lce_plan", "ikbo_lce_forward", "ikbo_lce_backward", "ikbo_lce_check", "ikbo_lce_plan_info",
+EXPORTED = ("ikbo_lce_plan", "ikbo_lce_forward", "ikbo_lce_backward", "ikbo_lce_check",
+            "ikbo_fa_plan", "ikbo_fa_forward", "ikbo_fa_check", "ikbo_fa_plan_destroy", "ikbo_lce_plan_info",
             "ikbo_lce_plan_set_spin_limit", "ikbo_lce_plan_destroy", "ikbo_status_str",
             "ikbo_last_error_message")
 
@@ -70,6 +74,14 @@ def lib() -> ctypes.CDLL:
         L.ikbo_lce_forward.restype = ip
         L.ikbo_lce_backward.argtypes = [vp] + [vp] * 10 + [i] * 6 + [vp]
         L.ikbo_lce_backward.restype = ip
+        L.ikbo_fa_plan.argtypes = [ctypes.POINTER(vp), i, i, i, i, i, i, i, ctypes.c_uint]
+        L.ikbo_fa_plan.restype = ip
+        L.ikbo_fa_forward.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, ctypes.c_float, vp]
+        L.ikbo_fa_forward.restype = ip
+        L.ikbo_fa_check.argtypes = [vp, vp]
+        L.ikbo_fa_check.restype = ip
+        L.ikbo_fa_plan_destroy.argtypes = [vp]
+        L.ikbo_fa_plan_destroy.restype = ip
         L.ikbo_lce_check.argtypes = [vp, vp]
         L.ikbo_lce_check.restype = ip
         L.ikbo_lce_plan_info.argtypes = [vp, ctypes.c_char_p, sz]
@@ -225,6 +237,80 @@ class LcePlan:
             self._h = None
             if st != IKBO_OK:
                 raise IkboError(st, "ikbo_lce_plan_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+class FaPlan:
+    """A plan for IKBO target attention (see ``ikbo_fa_plan``): the queries of each
+    candidate attend over the keys and values of its user, which are never replicated."""
+
+    def __init__(self, max_B_u: int, max_B_c: int, H: int, L_q: int, L_kv: int, head_dim: int,
+                 dtype: str = "bf16"):
+        self.dims = (H, L_q, L_kv, head_dim)
+        self.max_B_u, self.max_B_c = max_B_u, max_B_c
+        h = ctypes.c_void_p()
+        st = lib().ikbo_fa_plan(ctypes.byref(h), max_B_u, max_B_c, H, L_q, L_kv, head_dim, DTYPES[dtype], 0)
+        if st != IKBO_OK:
+            raise IkboError(st, "ikbo_fa_plan")
+        self._h = h
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise ValueError("plan destroyed")
+        return self._h
+
+    def forward_ptrs(self, Q: int, K: int, V: int, mp: int, O: int, B_u: int, B_c: int, scale: float = 0.0,
+                     stream: Optional[int] = None) -> int:
+        """Raw C-ABI call on device pointers; returns the status code."""
+        H, L_q, L_kv, hd = self.dims
+        return lib().ikbo_fa_forward(self.handle, Q, K, V, mp, O, B_u, B_c, H, L_q, L_kv, hd, float(scale), stream)
+
+    def forward(self, Q, K, V, mp, out=None, scale: float = 0.0, stream=None):
+        """O = softmax(scale Q K[map]^T) V[map] per head on the current (or given) stream."""
+        torch = _torch()
+        for name, t in (("Q", Q), ("K", K), ("V", V)):
+            if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bfloat16 tensor on the GPU")
+        if mp.dtype != torch.int32:
+            mp = mp.to(torch.int32)
+        mp = mp.contiguous()
+        H, L_q, L_kv, hd = self.dims
+        B_c, B_u = Q.shape[0], K.shape[0]
+        if tuple(Q.shape) != (B_c, H, L_q, hd) or tuple(K.shape) != (B_u, H, L_kv, hd) or K.shape != V.shape \
+                or mp.shape != (B_c,):
+            raise IkboError(IKBO_ERR_INVALID_ARG, "shape differs from the plan")
+        if out is None:
+            out = torch.empty_like(Q)
+        elif out.dtype != torch.bfloat16 or not out.is_contiguous() or out.shape != Q.shape:
+            raise ValueError("out must be a contiguous bfloat16 tensor shaped like Q")
+        st = self.forward_ptrs(Q.data_ptr(), K.data_ptr(), V.data_ptr(), mp.data_ptr(), out.data_ptr(), B_u, B_c,
+                               scale, _stream_handle(stream))
+        if st != IKBO_OK:
+            raise IkboError(st, "ikbo_fa_forward")
+        return out
+
+    def check(self, stream=None) -> int:
+        """Synchronise and return (and clear) the device-side status."""
+        return lib().ikbo_fa_check(self.handle, _stream_handle(stream))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            st = lib().ikbo_fa_plan_destroy(self._h)
+            self._h = None
+            if st != IKBO_OK:
+                raise IkboError(st, "ikbo_fa_plan_destroy")
 
     def __del__(self):
         try:

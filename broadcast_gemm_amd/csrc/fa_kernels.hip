@@ -1,0 +1,276 @@
+// fa_kernels.hip -- IKBO target attention forward on gfx950.
+//
+// The queries of candidate b attend over the keys and values of its user u = map[b], head
+// by head: O[b,h] = softmax(scale * Q[b,h] K[u,h]^T) V[u,h] (IKBO recsys blog, "Deep Dive:
+// Flash Attention").  The broadcast K and V are never materialised: the candidates of a
+// user share one copy, and a block computes up to kFaGroup of them (one wave each) for one
+// head, so every K/V block it stages in LDS serves all of them.  Blocks are launched with
+// the candidate groups before the heads, so that the blocks running together read the
+// same user's K/V (the pages' grid order for L2 reuse).
+//
+// A wave holds its candidate's 16*QT query rows.  With v_mfma_f32_16x16x32_bf16 it forms
+// the transposed scores S^T = K Q^T (A: key rows from LDS; B: query rows in registers),
+// so lane (g, j) ends up with the scores of query j against keys 4g .. 4g+3 of every
+// 16-key tile.  Those are exactly the values it must supply for O^T = V^T P^T (B operand
+// P^T: query j, 8 keys), once the k slots of each 32-key step are taken as keys
+// 4g .. 4g+3 and 16+4g .. 16+4g+3: no data moves between lanes for P.  V^T's fragments
+// (A operand: one d row, the same 8 keys) are two 8-byte LDS reads, because V is written
+// into LDS transposed when it is staged.  The output O^T leaves lane (g, j) with query j,
+// so the running maximum, the rescaling of O and the row sums are lane-local; only the
+// block maximum is reduced across the four lane groups.  Softmax runs in base 2 (scores
+// scaled by scale * log2 e, v_exp_f32), with the running maximum subtracted.
+#include "fa_internal.h"
+#include "ikbo_group.h"
+#include "lce_rowtile.h"
+
+namespace ikbo {
+
+namespace {
+
+__global__ void __launch_bounds__(kFaPrepBlock) fa_prep_kernel(FaPrepArgs a) {
+    extern __shared__ int sh[];
+    group_by_user(a.map, a.B_u, a.B_c, a.perm, nullptr, a.off, a.err, sh);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int *offs = sh + (size_t)((a.B_c + 63) / 64) * a.B_u;
+        int run = 0;
+        for (int u = 0; u < a.B_u; ++u) {
+            a.goff[u] = run;
+            run += (offs[u + 1] - offs[u] + kFaGroup - 1) / kFaGroup;
+        }
+        a.goff[a.B_u] = run;
+    }
+}
+
+template <int HD>
+struct FaLds {
+    static constexpr int KROW = HD * 2 + 16;        // bytes per staged K row (padded)
+    static constexpr int VROW = kFaKeys * 2 + 16;   // bytes per staged V^T row (padded)
+    static constexpr int KBYTES = kFaKeys * KROW;
+    static constexpr int BUF = KBYTES + HD * VROW;  // one K block and one V^T block
+    static constexpr int CHUNKS = kFaKeys * HD / 8 / 256;   // 16-byte chunks per thread per block
+};
+
+__device__ __forceinline__ float wave_max4(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float wave_sum4(float x) {
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+
+template <int QT, int HD>
+__global__ void __launch_bounds__(256, 1) fa_fwd_kernel(FaArgs a) {
+    using L = FaLds<HD>;
+    constexpr int TK = HD / 32;   // 32-column steps of d
+    constexpr int DT = HD / 16;   // 16-row tiles of O^T
+    extern __shared__ __align__(16) char lds[];
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int g = lane >> 4, j = lane & 15;
+    const int gi = (int)blockIdx.x % a.n_groups_max, h = (int)blockIdx.x / a.n_groups_max;
+    if (gi >= a.goff[a.B_u]) return;   // the whole block: no barrier has run
+    // The user of group gi: the last u with goff[u] <= gi (users without candidates share
+    // their successor's goff and are skipped).
+    int lo = 0, hi = a.B_u;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.goff[mid] <= gi) lo = mid;
+        else hi = mid;
+    }
+    const int u = lo;
+    const int first = a.off[u] + (gi - a.goff[u]) * kFaGroup;
+    const bool active = first + wv < a.off[u + 1];
+    const int b = active ? a.perm[first + wv] : 0;
+
+    const size_t kv0 = ((size_t)u * a.H + h) * a.L_kv * HD;
+    const __amdgpu_buffer_rsrc_t rsK = uniform_rsrc(a.K + kv0, a.L_kv * HD * 2);
+    const __amdgpu_buffer_rsrc_t rsV = uniform_rsrc(a.V + kv0, a.L_kv * HD * 2);
+
+    // Query fragments (B operand of S^T): lane (g, j) holds query 16*qt + j, d = 32t + 8g ...
+    u32x4_t qf[QT][TK];
+    {
+        const __amdgpu_buffer_rsrc_t rsQ =
+            uniform_rsrc(active ? a.Q + ((size_t)b * a.H + h) * a.L_q * HD : nullptr, active ? a.L_q * HD * 2 : 0);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+            for (int t = 0; t < TK; ++t)
+                qf[qt][t] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsQ, ((16 * qt + j) * HD + 32 * t + 8 * g) * 2, 0, 0));
+    }
+
+    // Staging: chunk c of a block is key c / (HD/8), columns 8 * (c % (HD/8)) .. +7.
+    u32x4_t kst[L::CHUNKS], vst[L::CHUNKS];
+    auto load_block = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < L::CHUNKS; ++i) {
+            const int c = tid + 256 * i;
+            const int off = ((kb * kFaKeys + c / (HD / 8)) * HD + 8 * (c % (HD / 8))) * 2;
+            kst[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsK, off, 0, 0));
+            vst[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsV, off, 0, 0));
+        }
+    };
+    auto store_block = [&](int buf) {
+        char *Kl = lds + buf * L::BUF;
+        char *Vl = Kl + L::KBYTES;
+#pragma unroll
+        for (int i = 0; i < L::CHUNKS; ++i) {
+            const int c = tid + 256 * i;
+            const int key = c / (HD / 8), d0 = 8 * (c % (HD / 8));
+            *reinterpret_cast<u32x4_t *>(Kl + key * L::KROW + d0 * 2) = kst[i];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t w = vst[i][e >> 1];
+                *reinterpret_cast<uint16_t *>(Vl + (d0 + e) * L::VROW + key * 2) =
+                    (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+            }
+        }
+    };
+
+    f32x4_t oacc[DT][QT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    float m[QT], l[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        m[qt] = -__builtin_inff();
+        l[qt] = 0.0f;
+    }
+
+    const int n_kb = (a.L_kv + kFaKeys - 1) / kFaKeys;
+    load_block(0);
+    store_block(0);
+    __syncthreads();
+    for (int kb = 0; kb < n_kb; ++kb) {
+        const bool more = kb + 1 < n_kb;
+        if (more) load_block(kb + 1);
+        if (active) {
+            const char *Kl = lds + (kb & 1) * L::BUF;
+            const char *Vl = Kl + L::KBYTES;
+            // S^T tiles: keys 16*kt + 4g + i (rows) against queries 16*qt + j (columns).
+            f32x4_t st[4][QT];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) st[kt][qt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < TK; ++t) {
+                    const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(Kl + (16 * kt + j) * L::KROW + (32 * t + 8 * g) * 2);
+#pragma unroll
+                    for (int qt = 0; qt < QT; ++qt) st[kt][qt] = mfma_bf16(kf, qf[qt][t], st[kt][qt]);
+                }
+            }
+            const int key0 = kb * kFaKeys + 4 * g;
+            u32x4_t pf[2][QT];
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) {
+                float mx = -__builtin_inff();
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = st[kt][qt][i] * a.scale_log2;
+                        if (key0 + 16 * kt + i >= a.L_kv) v = -__builtin_inff();
+                        st[kt][qt][i] = v;
+                        mx = fmaxf(mx, v);
+                    }
+                const float mnew = fmaxf(m[qt], wave_max4(mx));
+                const float alpha = __builtin_amdgcn_exp2f(m[qt] - mnew);
+                m[qt] = mnew;
+                float ls = 0.0f;
+                float p[4][4];
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        p[kt][i] = __builtin_amdgcn_exp2f(st[kt][qt][i] - mnew);
+                        ls += p[kt][i];
+                    }
+                l[qt] = l[qt] * alpha + ls;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    pf[s][qt] = (u32x4_t){pack_bf16x2(p[2 * s][0], p[2 * s][1]), pack_bf16x2(p[2 * s][2], p[2 * s][3]),
+                                          pack_bf16x2(p[2 * s + 1][0], p[2 * s + 1][1]),
+                                          pack_bf16x2(p[2 * s + 1][2], p[2 * s + 1][3])};
+            }
+            // O^T += V^T P^T: d rows 16*dt + j, key slots (32s + 4g .. +3, 32s + 16 + 4g .. +3).
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const char *row = Vl + (16 * dt + j) * L::VROW;
+                    const u32x2_t v0 = *reinterpret_cast<const u32x2_t *>(row + (32 * s + 4 * g) * 2);
+                    const u32x2_t v1 = *reinterpret_cast<const u32x2_t *>(row + (32 * s + 16 + 4 * g) * 2);
+                    const u32x4_t vf = (u32x4_t){v0[0], v0[1], v1[0], v1[1]};
+#pragma unroll
+                    for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = mfma_bf16(vf, pf[s][qt], oacc[dt][qt]);
+                }
+        }
+        if (more) store_block((kb + 1) & 1);
+        __syncthreads();
+    }
+    if (!active) return;
+    // O[b, h, 16*qt + j, 16*dt + 4g .. +3] = O^T / row sum.
+    uint16_t *ob = a.O + ((size_t)b * a.H + h) * a.L_q * HD;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        const float inv = 1.0f / wave_sum4(l[qt]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const f32x4_t o = oacc[dt][qt];
+            const u32x2_t w = (u32x2_t){pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+            *reinterpret_cast<u32x2_t *>(ob + (size_t)(16 * qt + j) * HD + 16 * dt + 4 * g) = w;
+        }
+    }
+}
+
+template <int QT, int HD>
+hipError_t launch_qt(const FaArgs &a, hipStream_t s) {
+    const auto k = fa_fwd_kernel<QT, HD>;
+    const size_t lds = 2 * (size_t)FaLds<HD>::BUF;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3((unsigned)(a.n_groups_max * a.H)), dim3(256), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int HD>
+hipError_t launch_hd(const FaArgs &a, hipStream_t s) {
+    switch (a.L_q) {
+        case 16: return launch_qt<1, HD>(a, s);
+        case 32: return launch_qt<2, HD>(a, s);
+        case 64: return launch_qt<4, HD>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t fa_prep_lds_bytes(int B_u, int B_c) { return group_lds_ints(B_u, B_c) * sizeof(int); }
+
+hipError_t launch_fa_prep(const FaPrepArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(fa_prep_kernel, dim3(1), dim3(kFaPrepBlock), fa_prep_lds_bytes(a.B_u, a.B_c), s, a);
+    return hipGetLastError();
+}
+
+size_t fa_lds_bytes(int hd) {
+    return hd == 128 ? 2 * (size_t)FaLds<128>::BUF : hd == 64 ? 2 * (size_t)FaLds<64>::BUF : 0;
+}
+
+hipError_t launch_fa_forward(const FaArgs &a, hipStream_t s) {
+    if (a.n_groups_max == 0) return hipSuccess;
+    switch (a.hd) {
+        case 64: return launch_hd<64>(a, s);
+        case 128: return launch_hd<128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ikbo

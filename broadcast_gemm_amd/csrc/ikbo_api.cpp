@@ -19,6 +19,7 @@
 #include <new>
 #include <string>
 
+#include "fa_internal.h"
 #include "lce_internal.h"
 #include "lce_rowtile.h"
 
@@ -71,10 +72,14 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int hip_fail(hipError_t e, const char *what) {
+}  // namespace
+
+int ikbo::hip_fail(hipError_t e, const char *what) {
     g_last_error = std::string(what) + ": " + hipGetErrorString(e);
     return IKBO_ERR_HIP;
 }
+
+namespace {
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

@@ -30,6 +30,7 @@
 //
 // dC and dU run on the forward's engines (ikbo_api.cpp): the row-tile engine with
 // W_c^T staged in LDS, and the flat engine with [W_u^T | W_u^T] against [S_hi; S_lo].
+#include "ikbo_group.h"
 #include "lce_internal.h"
 #include "lce_rowtile.h"
 
@@ -49,83 +50,10 @@ __device__ __forceinline__ float round_bf16(float x) {
 
 // ---- prep ---------------------------------------------------------------------------------
 
-// Block 0: stable grouping of the candidates by user.  The candidates are taken in
-// groups of 64 (one wave-wide ballot each).  cnt[g][u] counts the candidates of user u
-// in group g, then becomes the number of user-u candidates in groups before g; with
-// the user offsets that places candidate b at off[u] + cnt[g][u] + (its rank among the
-// user-u lanes of its group), which keeps ascending b within a user.  Entries outside
-// [0, B_u) set ERRBIT_MAP and are left out (off[B_u] counts the valid ones).
-__device__ void group_by_user(const BwdPrepArgs &a) {
-    extern __shared__ int sh[];
-    const int B_u = a.B_u, B_c = a.B_c;
-    const int G = (B_c + 63) / 64;
-    int *cnt = sh;                    // [G][B_u]
-    int *offs = sh + G * B_u;         // [B_u + 1]
-    const int tid = (int)threadIdx.x, nt = (int)blockDim.x;
-    const int lane = tid & 63, wv = tid >> 6, nw = nt >> 6;
-    const uint64_t below = (1ull << lane) - 1ull;
-    for (int i = tid; i < G * B_u; i += nt) cnt[i] = 0;
-    __syncthreads();
-    for (int gi = wv; gi < G; gi += nw) {
-        const int b = gi * 64 + lane;
-        const int u = b < B_c ? a.map[b] : 0;
-        const bool valid = b < B_c && u >= 0 && u < B_u;
-        if (b < B_c && !valid) atomicOr(a.err, ERRBIT_MAP);
-        uint64_t rem = __ballot(valid);
-        while (rem) {
-            const int leader = __ffsll((unsigned long long)rem) - 1;
-            const int lu = __shfl(u, leader);
-            const uint64_t m = __ballot(valid && u == lu);
-            if (lane == leader) cnt[gi * B_u + lu] = __popcll(m);
-            rem &= ~m;
-        }
-    }
-    __syncthreads();
-    for (int u = tid; u < B_u; u += nt) {
-        int run = 0;
-        for (int gi = 0; gi < G; ++gi) {
-            const int t = cnt[gi * B_u + u];
-            cnt[gi * B_u + u] = run;
-            run += t;
-        }
-        offs[u] = run;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int u = 0; u < B_u; ++u) {
-            const int t = offs[u];
-            offs[u] = run;
-            run += t;
-        }
-        offs[B_u] = run;
-    }
-    __syncthreads();
-    for (int u = tid; u <= B_u; u += nt) a.off[u] = offs[u];
-    for (int gi = wv; gi < G; gi += nw) {
-        const int b = gi * 64 + lane;
-        const int u = b < B_c ? a.map[b] : 0;
-        const bool valid = b < B_c && u >= 0 && u < B_u;
-        uint64_t rem = __ballot(valid);
-        int rank = 0;
-        while (rem) {
-            const int leader = __ffsll((unsigned long long)rem) - 1;
-            const int lu = __shfl(u, leader);
-            const uint64_t m = __ballot(valid && u == lu);
-            if (valid && u == lu) rank = __popcll(m & below);
-            rem &= ~m;
-        }
-        if (valid) {
-            const int pos = offs[u] + cnt[gi * B_u + u] + rank;
-            a.perm[pos] = b;
-            a.su[pos] = u;
-        }
-    }
-}
-
 __global__ void __launch_bounds__(kBwdPrepBlock) bwd_prep_kernel(BwdPrepArgs a) {
     if (blockIdx.x == 0) {
-        group_by_user(a);
+        extern __shared__ int sh[];
+        group_by_user(a.map, a.B_u, a.B_c, a.perm, a.su, a.off, a.err, sh);
         return;
     }
     // W_c^T [K_c][M] and [W_u^T | W_u^T] ([K_u] rows of ldw_dup elements; the padding was
@@ -389,7 +317,7 @@ int grid_for(long long work, int per_block) {
 }  // namespace
 
 size_t bwd_prep_lds_bytes(int B_u, int B_c) {
-    return ((size_t)((B_c + 63) / 64) * B_u + B_u + 1) * sizeof(int);
+    return group_lds_ints(B_u, B_c) * sizeof(int);
 }
 
 hipError_t launch_bwd_prep(const BwdPrepArgs &a, hipStream_t s) {

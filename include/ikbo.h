@@ -170,6 +170,45 @@ int ikbo_lce_plan_set_spin_limit(ikbo_lce_plan_t plan, uint32_t max_polls);
 /* Free the plan and its workspace (synchronises the device first).  NULL is a no-op. */
 int ikbo_lce_plan_destroy(ikbo_lce_plan_t plan);
 
+/*
+ * IKBO target attention (IKBO recsys blog, "Deep Dive: Flash Attention"): the queries of
+ * each candidate attend over the keys and values of its user,
+ *
+ *     O[b,h] = softmax(scale * Q[b,h] . K[map[b],h]^T) . V[map[b],h]      for b < B_c, h < H
+ *
+ * with K and V at the user batch B_u, never replicated per candidate.  Layouts (device
+ * memory owned by the caller, dense row-major, bf16):
+ *     Q, O [B_c, H, L_q, head_dim]      K, V [B_u, H, L_kv, head_dim]      map [B_c] int32
+ * Scores, softmax and the weighted sum accumulate in float32 (the softmax weights reach
+ * the matrix cores as bf16); O is rounded to bf16 once.  No mask: every query sees all
+ * L_kv keys of its user.
+ *
+ * ikbo_fa_plan: fixed H, L_q, L_kv, head_dim; bf16 only, head_dim 64 or 128, L_q 16, 32
+ * or 64 (one wave holds a candidate's queries); any L_kv >= 1.  flags must be 0.
+ * Allocates a small workspace (the candidates grouped by user) on the current device.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+typedef struct ikbo_fa_plan_s *ikbo_fa_plan_t;
+int ikbo_fa_plan(ikbo_fa_plan_t *plan, int max_B_u, int max_B_c, int H, int L_q, int L_kv, int head_dim,
+                 int dtype, unsigned flags);
+
+/*
+ * Enqueue the attention on `stream`.  scale = 0 means 1/sqrt(head_dim); a negative, NaN or
+ * infinite scale is INVALID_ARG.  Q, K, V and O must be 16-byte aligned, map 4-byte.
+ * B_c = 0 is a no-op.  Asynchronous: map entries outside [0, B_u) leave their candidates'
+ * O unwritten and are reported by ikbo_fa_check as IKBO_ERR_MAP_RANGE.  One plan serves
+ * one stream at a time.
+ */
+int ikbo_fa_forward(ikbo_fa_plan_t plan, const void *Q, const void *K, const void *V, const int32_t *map,
+                    void *O, int B_u, int B_c, int H, int L_q, int L_kv, int head_dim, float scale,
+                    void *stream);
+
+/* Wait for `stream`, then return and clear the device status (IKBO_OK or IKBO_ERR_MAP_RANGE). */
+int ikbo_fa_check(ikbo_fa_plan_t plan, void *stream);
+
+/* Free the plan and its workspace (synchronises the device first).  NULL is a no-op. */
+int ikbo_fa_plan_destroy(ikbo_fa_plan_t plan);
+
 /* Static text for a status code. */
 const char *ikbo_status_str(int status);
 

@@ -104,3 +104,16 @@ def test_backward_rejects_bad_arguments_before_hip(L):
     assert h.value is None
     # No plan: rejected before any HIP call.
     assert L.ikbo_lce_backward(None, *([None] * 10), 1, 1, 13, 11, 8, 16, None) == bga.IKBO_ERR_INVALID_ARG
+
+
+def test_fa_rejects_bad_arguments_before_hip(L):
+    h = ctypes.c_void_p()
+    bad_args = [(0, 8, 4, 64, 100, 128, 0, 0), (2, 8, 4, 64, 100, 128, 0, 1), (2, 8, 0, 64, 100, 128, 0, 0)]
+    for args in bad_args:
+        assert L.ikbo_fa_plan(ctypes.byref(h), *args) == bga.IKBO_ERR_INVALID_ARG, args
+    unsupported = [(2, 8, 4, 64, 100, 96, 0, 0), (2, 8, 4, 48, 100, 128, 0, 0), (2, 8, 4, 64, 100, 128, 1, 0)]
+    for args in unsupported:
+        assert L.ikbo_fa_plan(ctypes.byref(h), *args) == bga.IKBO_ERR_UNSUPPORTED, args
+    assert h.value is None
+    assert L.ikbo_fa_forward(None, None, None, None, None, None, 1, 1, 4, 64, 100, 128, 0.0, None) == \
+        bga.IKBO_ERR_INVALID_ARG
