@@ -355,6 +355,114 @@ def run_backward(args, cfg, x) -> int:
     return 0
 
 
+def fa_flops(c) -> int:
+    """Q K^T and P V: 2 flops per multiply-add, 2 products."""
+    return 4 * c.B_c * c.H * c.L_q * c.L_kv * c.hd
+
+
+def fa_bytes(c) -> int:
+    """Q read and O written per candidate; K and V read once per user; the map."""
+    return 2 * (2 * c.B_c * c.H * c.L_q * c.hd + 2 * c.B_u * c.H * c.L_kv * c.hd) + 4 * c.B_c
+
+
+def run_fa(args) -> int:
+    """IKBO target attention: K forwards back to back on rotated buffer sets."""
+    import numpy as np
+    import torch
+
+    import broadcast_gemm_amd as bga
+    from broadcast_gemm_amd.inputs import FA_CONFIG_BY_NAME, bf16_bits_to_f32, make_fa_inputs
+
+    name = args.config if args.config in FA_CONFIG_BY_NAME else "fa-70to1"
+    c = FA_CONFIG_BY_NAME[name]
+    torch.cuda.set_device(0)
+    print(f"[bench] attention config={c.name} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    x = make_fa_inputs(c)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    base = [dev(a) for a in (x.Q, x.K, x.V, x.map)]
+    set_bytes = sum(t.numel() * t.element_size() for t in base) + base[0].numel() * 2
+    n_sets = max(1, math.ceil(args.rotate_mb * 2**20 / set_bytes))
+    sets = [(base if i == 0 else [t.clone() for t in base]) + [torch.empty_like(base[0])] for i in range(n_sets)]
+    plan = bga.FaPlan(c.B_u, c.B_c, c.H, c.L_q, c.L_kv, c.hd)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(i):
+        Q, K, V, mp, O = sets[i % n_sets]
+        st = plan.forward_ptrs(Q.data_ptr(), K.data_ptr(), V.data_ptr(), mp.data_ptr(), O.data_ptr(), c.B_u, c.B_c,
+                               0.0, sh)
+        if st != bga.IKBO_OK:
+            raise bga.IkboError(st, "ikbo_fa_forward")
+
+    for i in range(args.warmup):
+        step(i)
+    st = plan.check()
+    if st != bga.IKBO_OK:
+        raise bga.IkboError(st, "warmup device status")
+    K = args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(K):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    st = plan.check()
+    if st != bga.IKBO_OK:
+        raise bga.IkboError(st, "timed device status")
+    ms = t0.elapsed_time(t1) / K
+    flops, nbytes = fa_flops(c), fa_bytes(c)
+    tflops = flops / (ms * 1e-3) / 1e12
+    parity = None
+    out = {
+        "metric": "IKBO target attention TFLOP/s at B_c=1024, 70:1 (L_q=64, L_kv=1024, H=4, head_dim=128)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c.dtype, "data": "synthetic",
+        "config": {"workload": c.name, "B_u": c.B_u, "B_c": c.B_c, "H": c.H, "L_q": c.L_q, "L_kv": c.L_kv,
+                   "head_dim": c.hd, "map": c.map_kind, "rotating_sets": n_sets, "parallelism": "single GPU"},
+        "us_per_forward": round(ms * 1e3, 3),
+        "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
+        "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+        "arithmetic_intensity": round(flops / nbytes, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "fa_fwd_kernel (plus the one-block grouping launch)"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        O = sets[0][4]
+        On = bf16_bits_to_f32(O.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+        rng = np.random.default_rng(7)
+        rows = [(int(b), int(rng.integers(0, c.H)), int(rng.integers(0, c.L_q))) for b in rng.integers(0, c.B_c, 64)]
+        ref = oracle.fa_f64(x.Q, x.K, x.V, x.map, rows=rows)
+        nbad, _ = oracle.tolerance_violations(np.stack([On[r] for r in rows]), ref)
+        out["parity"] = {"rows_checked": len(rows), "violations": nbad}
+        # The oracle on a bounded sample: query rows one by one, for about cpu_seconds.
+        threads = oracle.max_threads()
+        sample = [(int(b), int(rng.integers(0, c.H)), int(rng.integers(0, c.L_q))) for b in rng.integers(0, c.B_c, 4096)]
+        reps, c0 = 0, time.perf_counter()
+        while True:
+            oracle.fa_f64(x.Q, x.K, x.V, x.map, rows=sample, threads=threads)
+            reps += 1
+            el = time.perf_counter() - c0
+            if el >= args.cpu_seconds or reps >= 1000:
+                break
+        row_flops = 4 * c.L_kv * c.hd
+        out["cpu_baseline"] = {"value": round(row_flops * len(sample) * reps / el / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"{len(sample)} random query rows of {c.name} x {reps}, fp64, K/V copied "
+                                         f"per row; {el:.1f} s wall"}
+    plan.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def run_copy(args) -> int:
     """Plain device copy of known size (calibrates FETCH_SIZE/WRITE_SIZE counters)."""
     import torch
@@ -378,7 +486,7 @@ def main() -> int:
     ap.add_argument("--rotate-mb", type=int, default=1100, help="total size of rotated buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--mode", default="lce", choices=["lce", "copy", "traffic", "rewrite", "backward"])
+    ap.add_argument("--mode", default="lce", choices=["lce", "copy", "traffic", "rewrite", "backward", "fa"])
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="--mode traffic: rocprofv3 --pmc output directories")
@@ -400,6 +508,8 @@ def main() -> int:
 
     if args.mode == "copy":
         return run_copy(args)
+    if args.mode == "fa":
+        return run_fa(args)
 
     import broadcast_gemm_amd as bga
     from broadcast_gemm_amd.inputs import CONFIG_BY_NAME, bf16_bits_to_f32, make_inputs

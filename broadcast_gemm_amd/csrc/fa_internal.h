@@ -15,19 +15,24 @@ constexpr int kFaGroup = 4;       // candidates of one user per block (one wave 
 constexpr int kFaKeys = 64;       // keys per staged K/V block
 constexpr int kFaPrepBlock = 1024;
 
-// Candidates grouped by user (perm, off) and the per-user count of blocks of kFaGroup.
+// Block 0: the candidates grouped by user (perm, off) and the per-user count of blocks of
+// kFaGroup (goff).  Blocks 1..: V transposed per (user, head) into Vt [B_u][H][hd][L_kv_pad]
+// (L_kv_pad = L_kv rounded up to kFaKeys; the padding is written as zeros).
 struct FaPrepArgs {
     const int32_t *map;
     int32_t *perm, *off, *goff;   // [B_c], [B_u + 1], [B_u + 1]
     uint32_t *err;
-    int B_u, B_c;
+    const uint16_t *V;            // [B_u][H][L_kv][hd]
+    uint16_t *Vt;                 // [B_u][H][hd][L_kv_pad]
+    int B_u, B_c, H, L_kv, hd;
 };
-size_t fa_prep_lds_bytes(int B_u, int B_c);
+size_t fa_prep_lds_bytes(int B_u, int B_c, int hd);
 hipError_t launch_fa_prep(const FaPrepArgs &a, hipStream_t s);
 
 struct FaArgs {
     const uint16_t *Q;            // [B_c][H][L_q][hd]
-    const uint16_t *K, *V;        // [B_u][H][L_kv][hd]
+    const uint16_t *K;            // [B_u][H][L_kv][hd]
+    const uint16_t *Vt;           // [B_u][H][hd][L_kv_pad]
     uint16_t *O;                  // [B_c][H][L_q][hd]
     const int32_t *perm, *off, *goff;
     int B_u, H, L_q, L_kv, hd;

@@ -8,7 +8,8 @@
 // the candidate groups before the heads, so that the blocks running together read the
 // same user's K/V (the pages' grid order for L2 reuse).
 //
-// A wave holds its candidate's 16*QT query rows.  With v_mfma_f32_16x16x32_bf16 it forms
+// A wave holds 16*QT query rows of its candidate (a candidate's 64 queries take two waves,
+// so that everything a wave keeps stays within its share of the register file).  With v_mfma_f32_16x16x32_bf16 it forms
 // the transposed scores S^T = K Q^T (A: key rows from LDS; B: query rows in registers),
 // so lane (g, j) ends up with the scores of query j against keys 4g .. 4g+3 of every
 // 16-key tile.  Those are exactly the values it must supply for O^T = V^T P^T (B operand
@@ -19,6 +20,8 @@
 // so the running maximum, the rescaling of O and the row sums are lane-local; only the
 // block maximum is reduced across the four lane groups.  Softmax runs in base 2 (scores
 // scaled by scale * log2 e, v_exp_f32), with the running maximum subtracted.
+#include <algorithm>
+
 #include "fa_internal.h"
 #include "ikbo_group.h"
 #include "lce_rowtile.h"
@@ -29,27 +32,61 @@ namespace {
 
 __global__ void __launch_bounds__(kFaPrepBlock) fa_prep_kernel(FaPrepArgs a) {
     extern __shared__ int sh[];
-    group_by_user(a.map, a.B_u, a.B_c, a.perm, nullptr, a.off, a.err, sh);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int *offs = sh + (size_t)((a.B_c + 63) / 64) * a.B_u;
-        int run = 0;
-        for (int u = 0; u < a.B_u; ++u) {
-            a.goff[u] = run;
-            run += (offs[u + 1] - offs[u] + kFaGroup - 1) / kFaGroup;
+    if (blockIdx.x == 0) {
+        group_by_user(a.map, a.B_u, a.B_c, a.perm, nullptr, a.off, a.err, sh);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int *offs = sh + (size_t)((a.B_c + 63) / 64) * a.B_u;
+            int run = 0;
+            for (int u = 0; u < a.B_u; ++u) {
+                a.goff[u] = run;
+                run += (offs[u + 1] - offs[u] + kFaGroup - 1) / kFaGroup;
+            }
+            a.goff[a.B_u] = run;
         }
-        a.goff[a.B_u] = run;
+        return;
+    }
+    // One tile of 64 keys of one (user, head): V rows into LDS (row stride hd + 2 elements),
+    // then each thread gathers 8 keys of one d column and writes them as 16 bytes of Vt.
+    const int n_kb = (a.L_kv + kFaKeys - 1) / kFaKeys;
+    const int L_pad = n_kb * kFaKeys;
+    const int t = (int)blockIdx.x - 1;
+    const int kb = t % n_kb, uh = t / n_kb;
+    const int hd = a.hd, ld = a.hd + 2;
+    uint16_t *tile = reinterpret_cast<uint16_t *>(sh);
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(a.V + (size_t)uh * a.L_kv * hd, a.L_kv * hd * 2);
+    for (int c = (int)threadIdx.x; c < kFaKeys * hd / 8; c += (int)blockDim.x) {
+        const int key = c / (hd / 8), d0 = 8 * (c % (hd / 8));
+        const u32x4_t v = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, ((kb * kFaKeys + key) * hd + d0) * 2, 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<uint32_t *>(tile + key * ld + d0 + 2 * e) = v[e];
+    }
+    __syncthreads();
+    for (int c = (int)threadIdx.x; c < hd * (kFaKeys / 8); c += (int)blockDim.x) {
+        const int d = c / (kFaKeys / 8), k0 = 8 * (c % (kFaKeys / 8));
+        u32x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = (uint32_t)tile[(k0 + 2 * e) * ld + d] | ((uint32_t)tile[(k0 + 2 * e + 1) * ld + d] << 16);
+        *reinterpret_cast<u32x4_t *>(a.Vt + ((size_t)uh * hd + d) * L_pad + kb * kFaKeys + k0) = w;
     }
 }
 
-template <int HD>
+template <int HD, int NT>
 struct FaLds {
     static constexpr int KROW = HD * 2 + 16;        // bytes per staged K row (padded)
     static constexpr int VROW = kFaKeys * 2 + 16;   // bytes per staged V^T row (padded)
     static constexpr int KBYTES = kFaKeys * KROW;
     static constexpr int BUF = KBYTES + HD * VROW;  // one K block and one V^T block
-    static constexpr int CHUNKS = kFaKeys * HD / 8 / 256;   // 16-byte chunks per thread per block
+    static constexpr int CHUNKS = kFaKeys * HD / 8 / NT;   // 16-byte chunks per thread per block (NT threads)
+    static constexpr int QROW = HD * 2 + 16;        // bytes per staged query row (padded)
+    static constexpr int QWAVE = 64 * QROW / (NT / 64 / kFaGroup);   // one wave's query rows (64/WPC of them)
+    static constexpr int TOTAL = 2 * BUF + (NT / 64) * QWAVE;
 };
+
+constexpr float kFaSlack = 8.0f;   // log2 headroom of the weights before O is rescaled
 
 __device__ __forceinline__ float wave_max4(float x) {
     x = fmaxf(x, __shfl_xor(x, 16));
@@ -60,9 +97,11 @@ __device__ __forceinline__ float wave_sum4(float x) {
     return x + __shfl_xor(x, 32);
 }
 
-template <int QT, int HD>
-__global__ void __launch_bounds__(256, 1) fa_fwd_kernel(FaArgs a) {
-    using L = FaLds<HD>;
+// WPC waves per candidate, each with 16*QT of its queries; kFaGroup candidates per block.
+template <int QT, int WPC, int HD>
+__global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a) {
+    constexpr int NT = 64 * kFaGroup * WPC;
+    using L = FaLds<HD, NT>;
     constexpr int TK = HD / 32;   // 32-column steps of d
     constexpr int DT = HD / 16;   // 16-row tiles of O^T
     extern __shared__ __align__(16) char lds[];
@@ -81,35 +120,42 @@ __global__ void __launch_bounds__(256, 1) fa_fwd_kernel(FaArgs a) {
     }
     const int u = lo;
     const int first = a.off[u] + (gi - a.goff[u]) * kFaGroup;
-    const bool active = first + wv < a.off[u + 1];
-    const int b = active ? a.perm[first + wv] : 0;
+    const int cs = wv / WPC, q0 = 16 * QT * (wv % WPC);   // candidate slot, first query row
+    const bool active = first + cs < a.off[u + 1];
+    const int b = active ? a.perm[first + cs] : 0;
 
     const size_t kv0 = ((size_t)u * a.H + h) * a.L_kv * HD;
     const __amdgpu_buffer_rsrc_t rsK = uniform_rsrc(a.K + kv0, a.L_kv * HD * 2);
-    const __amdgpu_buffer_rsrc_t rsV = uniform_rsrc(a.V + kv0, a.L_kv * HD * 2);
 
-    // Query fragments (B operand of S^T): lane (g, j) holds query 16*qt + j, d = 32t + 8g ...
-    u32x4_t qf[QT][TK];
+    // The wave's queries go to its own LDS rows (read back as B-operand fragments: query
+    // 16*qt + j, d = 32t + 8g .. +7); a wave reads only what it wrote, so no barrier is needed.
+    char *Ql = lds + 2 * L::BUF + wv * L::QWAVE;
     {
         const __amdgpu_buffer_rsrc_t rsQ =
             uniform_rsrc(active ? a.Q + ((size_t)b * a.H + h) * a.L_q * HD : nullptr, active ? a.L_q * HD * 2 : 0);
+        constexpr int PER = 16 * QT * HD / 8 / 64;   // 16-byte chunks per lane
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-            for (int t = 0; t < TK; ++t)
-                qf[qt][t] = __builtin_bit_cast(
-                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsQ, ((16 * qt + j) * HD + 32 * t + 8 * g) * 2, 0, 0));
+        for (int i = 0; i < PER; ++i) {
+            const int c = lane + 64 * i;
+            const int row = c / (HD / 8), d0 = 8 * (c % (HD / 8));
+            *reinterpret_cast<u32x4_t *>(Ql + row * L::QROW + d0 * 2) = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsQ, ((q0 + row) * HD + d0) * 2, 0, 0));
+        }
     }
 
-    // Staging: chunk c of a block is key c / (HD/8), columns 8 * (c % (HD/8)) .. +7.
+    // Staging: K chunk c is key c / (HD/8), columns 8 * (c % (HD/8)) .. +7; V^T chunk c is
+    // d row c / 8, keys 8 * (c % 8) .. +7 of the block.
+    const int L_pad = ((a.L_kv + kFaKeys - 1) / kFaKeys) * kFaKeys;
+    const __amdgpu_buffer_rsrc_t rsV = uniform_rsrc(a.Vt + ((size_t)u * a.H + h) * HD * L_pad, HD * L_pad * 2);
     u32x4_t kst[L::CHUNKS], vst[L::CHUNKS];
     auto load_block = [&](int kb) {
 #pragma unroll
         for (int i = 0; i < L::CHUNKS; ++i) {
-            const int c = tid + 256 * i;
-            const int off = ((kb * kFaKeys + c / (HD / 8)) * HD + 8 * (c % (HD / 8))) * 2;
-            kst[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsK, off, 0, 0));
-            vst[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsV, off, 0, 0));
+            const int c = tid + NT * i;
+            kst[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rsK, ((kb * kFaKeys + c / (HD / 8)) * HD + 8 * (c % (HD / 8))) * 2, 0, 0));
+            vst[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rsV, ((c / 8) * L_pad + kb * kFaKeys + 8 * (c % 8)) * 2, 0, 0));
         }
     };
     auto store_block = [&](int buf) {
@@ -117,15 +163,9 @@ __global__ void __launch_bounds__(256, 1) fa_fwd_kernel(FaArgs a) {
         char *Vl = Kl + L::KBYTES;
 #pragma unroll
         for (int i = 0; i < L::CHUNKS; ++i) {
-            const int c = tid + 256 * i;
-            const int key = c / (HD / 8), d0 = 8 * (c % (HD / 8));
-            *reinterpret_cast<u32x4_t *>(Kl + key * L::KROW + d0 * 2) = kst[i];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t w = vst[i][e >> 1];
-                *reinterpret_cast<uint16_t *>(Vl + (d0 + e) * L::VROW + key * 2) =
-                    (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
-            }
+            const int c = tid + NT * i;
+            *reinterpret_cast<u32x4_t *>(Kl + (c / (HD / 8)) * L::KROW + 16 * (c % (HD / 8))) = kst[i];
+            *reinterpret_cast<u32x4_t *>(Vl + (c / 8) * L::VROW + 16 * (c % 8)) = vst[i];
         }
     };
 
@@ -142,78 +182,120 @@ __global__ void __launch_bounds__(256, 1) fa_fwd_kernel(FaArgs a) {
     }
 
     const int n_kb = (a.L_kv + kFaKeys - 1) / kFaKeys;
+    f32x4_t st[4][QT];
+    float mb[QT];
+    // S^T tiles for block kb: keys 16*kt + 4g + i (rows) against queries 16*qt + j (columns);
+    // keys past L_kv (only in a partial last block) score -inf.  Then the block maxima
+    // (base-2 scaled); returns whether some row's maximum exceeds the reference by more
+    // than kFaSlack (the same answer on every lane of the wave).
+    auto scores = [&](int kb) -> bool {
+        const char *Kl = lds + (kb & 1) * L::BUF;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) st[kt][qt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < TK; ++t) {
+            u32x4_t qf[QT];
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+                qf[qt] = *reinterpret_cast<const u32x4_t *>(Ql + (16 * qt + j) * L::QROW + (32 * t + 8 * g) * 2);
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(Kl + (16 * kt + j) * L::KROW + (32 * t + 8 * g) * 2);
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) st[kt][qt] = mfma_bf16(kf, qf[qt], st[kt][qt]);
+            }
+        }
+        if (kb == n_kb - 1 && (a.L_kv % kFaKeys) != 0) {
+            const int key0 = kb * kFaKeys + 4 * g;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (key0 + 16 * kt + i >= a.L_kv)
+#pragma unroll
+                        for (int qt = 0; qt < QT; ++qt) st[kt][qt][i] = -__builtin_inff();
+        }
+        bool grow = false;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[kt][qt][i]);
+            mb[qt] = wave_max4(mx) * a.scale_log2;
+            grow = grow || mb[qt] > m[qt] + kFaSlack;
+        }
+        return __builtin_amdgcn_readfirstlane(__ballot(grow) != 0 ? 1 : 0) != 0;
+    };
+    // Weights against the reference maximum (below 2^kFaSlack), row sums, and
+    // O^T += V^T P^T with d rows 16*dt + j and key slots (32s + 4g .. +3, 32s + 16 + 4g .. +3).
+    auto accumulate = [&](int kb) {
+        const char *Vl = lds + (kb & 1) * L::BUF + L::KBYTES;
+        u32x4_t pf[2][QT];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            const float nm = -m[qt];
+            float ls = 0.0f;
+            float p[4][4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[kt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][qt][i], a.scale_log2, nm));
+                    ls += p[kt][i];
+                }
+            l[qt] += ls;
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                pf[s][qt] = (u32x4_t){pack_bf16x2(p[2 * s][0], p[2 * s][1]), pack_bf16x2(p[2 * s][2], p[2 * s][3]),
+                                      pack_bf16x2(p[2 * s + 1][0], p[2 * s + 1][1]),
+                                      pack_bf16x2(p[2 * s + 1][2], p[2 * s + 1][3])};
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const char *row = Vl + (16 * dt + j) * L::VROW;
+                const u32x2_t v0 = *reinterpret_cast<const u32x2_t *>(row + (32 * s + 4 * g) * 2);
+                const u32x2_t v1 = *reinterpret_cast<const u32x2_t *>(row + (32 * s + 16 + 4 * g) * 2);
+                const u32x4_t vf = (u32x4_t){v0[0], v0[1], v1[0], v1[1]};
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = mfma_bf16(vf, pf[s][qt], oacc[dt][qt]);
+            }
+    };
+
+    // Every wave passes one barrier per key block on either path below.  The fast loop touches
+    // O only through the matrix cores; a block whose maximum grows (always the first, rarely a
+    // later one) leaves it and is finished by the rescaling path.
     load_block(0);
     store_block(0);
     __syncthreads();
-    for (int kb = 0; kb < n_kb; ++kb) {
-        const bool more = kb + 1 < n_kb;
-        if (more) load_block(kb + 1);
-        if (active) {
-            const char *Kl = lds + (kb & 1) * L::BUF;
-            const char *Vl = Kl + L::KBYTES;
-            // S^T tiles: keys 16*kt + 4g + i (rows) against queries 16*qt + j (columns).
-            f32x4_t st[4][QT];
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-                for (int qt = 0; qt < QT; ++qt) st[kt][qt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int t = 0; t < TK; ++t) {
-                    const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(Kl + (16 * kt + j) * L::KROW + (32 * t + 8 * g) * 2);
-#pragma unroll
-                    for (int qt = 0; qt < QT; ++qt) st[kt][qt] = mfma_bf16(kf, qf[qt][t], st[kt][qt]);
-                }
-            }
-            const int key0 = kb * kFaKeys + 4 * g;
-            u32x4_t pf[2][QT];
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt) {
-                float mx = -__builtin_inff();
-#pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float v = st[kt][qt][i] * a.scale_log2;
-                        if (key0 + 16 * kt + i >= a.L_kv) v = -__builtin_inff();
-                        st[kt][qt][i] = v;
-                        mx = fmaxf(mx, v);
-                    }
-                const float mnew = fmaxf(m[qt], wave_max4(mx));
-                const float alpha = __builtin_amdgcn_exp2f(m[qt] - mnew);
-                m[qt] = mnew;
-                float ls = 0.0f;
-                float p[4][4];
-#pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        p[kt][i] = __builtin_amdgcn_exp2f(st[kt][qt][i] - mnew);
-                        ls += p[kt][i];
-                    }
-                l[qt] = l[qt] * alpha + ls;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    pf[s][qt] = (u32x4_t){pack_bf16x2(p[2 * s][0], p[2 * s][1]), pack_bf16x2(p[2 * s][2], p[2 * s][3]),
-                                          pack_bf16x2(p[2 * s + 1][0], p[2 * s + 1][1]),
-                                          pack_bf16x2(p[2 * s + 1][2], p[2 * s + 1][3])};
-            }
-            // O^T += V^T P^T: d rows 16*dt + j, key slots (32s + 4g .. +3, 32s + 16 + 4g .. +3).
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const char *row = Vl + (16 * dt + j) * L::VROW;
-                    const u32x2_t v0 = *reinterpret_cast<const u32x2_t *>(row + (32 * s + 4 * g) * 2);
-                    const u32x2_t v1 = *reinterpret_cast<const u32x2_t *>(row + (32 * s + 16 + 4 * g) * 2);
-                    const u32x4_t vf = (u32x4_t){v0[0], v0[1], v1[0], v1[1]};
-#pragma unroll
-                    for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = mfma_bf16(vf, pf[s][qt], oacc[dt][qt]);
-                }
+    int kb = 0;
+    for (;;) {
+        for (; kb < n_kb; ++kb) {
+            if (kb + 1 < n_kb) load_block(kb + 1);
+            if (active && scores(kb)) break;
+            if (active) accumulate(kb);
+            if (kb + 1 < n_kb) store_block((kb + 1) & 1);
+            __syncthreads();
         }
-        if (more) store_block((kb + 1) & 1);
+        if (kb >= n_kb) break;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            const float mnew = fmaxf(m[qt], mb[qt]);
+            const float alpha = __builtin_amdgcn_exp2f(m[qt] - mnew);
+            m[qt] = mnew;
+            l[qt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+        }
+        accumulate(kb);
+        if (kb + 1 < n_kb) store_block((kb + 1) & 1);
         __syncthreads();
+        ++kb;
     }
     if (!active) return;
     // O[b, h, 16*qt + j, 16*dt + 4g .. +3] = O^T / row sum.
@@ -225,43 +307,48 @@ __global__ void __launch_bounds__(256, 1) fa_fwd_kernel(FaArgs a) {
         for (int dt = 0; dt < DT; ++dt) {
             const f32x4_t o = oacc[dt][qt];
             const u32x2_t w = (u32x2_t){pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
-            *reinterpret_cast<u32x2_t *>(ob + (size_t)(16 * qt + j) * HD + 16 * dt + 4 * g) = w;
+            *reinterpret_cast<u32x2_t *>(ob + (size_t)(q0 + 16 * qt + j) * HD + 16 * dt + 4 * g) = w;
         }
     }
 }
 
-template <int QT, int HD>
+template <int QT, int WPC, int HD>
 hipError_t launch_qt(const FaArgs &a, hipStream_t s) {
-    const auto k = fa_fwd_kernel<QT, HD>;
-    const size_t lds = 2 * (size_t)FaLds<HD>::BUF;
+    const auto k = fa_fwd_kernel<QT, WPC, HD>;
+    const size_t lds = (size_t)FaLds<HD, 64 * kFaGroup * WPC>::TOTAL;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3((unsigned)(a.n_groups_max * a.H)), dim3(256), lds, s, a);
+    hipLaunchKernelGGL(k, dim3((unsigned)(a.n_groups_max * a.H)), dim3(64 * kFaGroup * WPC), lds, s, a);
     return hipGetLastError();
 }
 
+// Queries per wave: 16 or 32 (two waves for a candidate's 64).
 template <int HD>
 hipError_t launch_hd(const FaArgs &a, hipStream_t s) {
     switch (a.L_q) {
-        case 16: return launch_qt<1, HD>(a, s);
-        case 32: return launch_qt<2, HD>(a, s);
-        case 64: return launch_qt<4, HD>(a, s);
+        case 16: return launch_qt<1, 1, HD>(a, s);
+        case 32: return launch_qt<2, 1, HD>(a, s);
+        case 64: return launch_qt<2, 2, HD>(a, s);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-size_t fa_prep_lds_bytes(int B_u, int B_c) { return group_lds_ints(B_u, B_c) * sizeof(int); }
+size_t fa_prep_lds_bytes(int B_u, int B_c, int hd) {
+    return std::max(group_lds_ints(B_u, B_c) * sizeof(int), (size_t)kFaKeys * (hd + 2) * 2);
+}
 
 hipError_t launch_fa_prep(const FaPrepArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(fa_prep_kernel, dim3(1), dim3(kFaPrepBlock), fa_prep_lds_bytes(a.B_u, a.B_c), s, a);
+    const long long tiles = (long long)a.B_u * a.H * ((a.L_kv + kFaKeys - 1) / kFaKeys);
+    hipLaunchKernelGGL(fa_prep_kernel, dim3((unsigned)(1 + tiles)), dim3(kFaPrepBlock),
+                       fa_prep_lds_bytes(a.B_u, a.B_c, a.hd), s, a);
     return hipGetLastError();
 }
 
 size_t fa_lds_bytes(int hd) {
-    return hd == 128 ? 2 * (size_t)FaLds<128>::BUF : hd == 64 ? 2 * (size_t)FaLds<64>::BUF : 0;
+    return hd == 128 ? (size_t)FaLds<128, 512>::TOTAL : hd == 64 ? (size_t)FaLds<64, 512>::TOTAL : 0;
 }
 
 hipError_t launch_fa_forward(const FaArgs &a, hipStream_t s) {

@@ -20,6 +20,7 @@ struct ikbo_fa_plan_s {
     size_t arena_bytes;
     int32_t *perm, *off, *goff;
     uint32_t *err;
+    uint16_t *Vt;                 // [max_B_u][H][head_dim][L_kv rounded up to kFaKeys]
 };
 
 namespace {
@@ -43,7 +44,7 @@ int ikbo_fa_plan(ikbo_fa_plan_t *out, int max_B_u, int max_B_c, int H, int L_q, 
         return IKBO_ERR_UNSUPPORTED;
     // Byte offsets within one (user, head) or (candidate, head) matrix are 32-bit; the grouping
     // table of the candidates fits one block's LDS.
-    if ((long long)L_kv * head_dim * 2 >= (1LL << 31) || fa_prep_lds_bytes(max_B_u, max_B_c) > 64 * 1024 ||
+    if ((long long)(L_kv + kFaKeys - 1) / kFaKeys * kFaKeys * head_dim * 2 >= (1LL << 31) || fa_prep_lds_bytes(max_B_u, max_B_c, head_dim) > 64 * 1024 ||
         (long long)((max_B_c + kFaGroup - 1) / kFaGroup + max_B_u) * H >= (1LL << 31))
         return IKBO_ERR_UNSUPPORTED;
     ikbo_fa_plan_s *p = new (std::nothrow) ikbo_fa_plan_s();
@@ -61,6 +62,8 @@ int ikbo_fa_plan(ikbo_fa_plan_t *out, int max_B_u, int max_B_c, int H, int L_q, 
     const size_t o_perm = take((size_t)std::max(max_B_c, 1) * 4);
     const size_t o_off = take((size_t)(max_B_u + 1) * 4);
     const size_t o_goff = take((size_t)(max_B_u + 1) * 4);
+    const size_t L_pad = (size_t)(L_kv + kFaKeys - 1) / kFaKeys * kFaKeys;
+    const size_t o_vt = take((size_t)max_B_u * H * head_dim * L_pad * 2);
     p->arena_bytes = off;
     e = hipMalloc(reinterpret_cast<void **>(&p->arena), p->arena_bytes);
     if (e != hipSuccess) { delete p; return hip_fail(e, "hipMalloc(workspace)"); }
@@ -70,6 +73,7 @@ int ikbo_fa_plan(ikbo_fa_plan_t *out, int max_B_u, int max_B_c, int H, int L_q, 
     p->perm = reinterpret_cast<int32_t *>(p->arena + o_perm);
     p->off = reinterpret_cast<int32_t *>(p->arena + o_off);
     p->goff = reinterpret_cast<int32_t *>(p->arena + o_goff);
+    p->Vt = reinterpret_cast<uint16_t *>(p->arena + o_vt);
     *out = p;
     return IKBO_OK;
 }
@@ -91,11 +95,12 @@ int ikbo_fa_forward(ikbo_fa_plan_t p, const void *Q, const void *K, const void *
     hipStream_t s = static_cast<hipStream_t>(stream);
     FaPrepArgs pa{};
     pa.map = map; pa.perm = p->perm; pa.off = p->off; pa.goff = p->goff; pa.err = p->err;
-    pa.B_u = B_u; pa.B_c = B_c;
+    pa.V = static_cast<const uint16_t *>(V); pa.Vt = p->Vt;
+    pa.B_u = B_u; pa.B_c = B_c; pa.H = H; pa.L_kv = L_kv; pa.hd = head_dim;
     if ((e = launch_fa_prep(pa, s)) != hipSuccess) return hip_fail(e, "fa prep");
     FaArgs a{};
     a.Q = static_cast<const uint16_t *>(Q); a.K = static_cast<const uint16_t *>(K);
-    a.V = static_cast<const uint16_t *>(V); a.O = static_cast<uint16_t *>(O);
+    a.Vt = p->Vt; a.O = static_cast<uint16_t *>(O);
     a.perm = p->perm; a.off = p->off; a.goff = p->goff;
     a.B_u = B_u; a.H = H; a.L_q = L_q; a.L_kv = L_kv; a.hd = head_dim;
     a.n_groups_max = (B_c + kFaGroup - 1) / kFaGroup + B_u;
