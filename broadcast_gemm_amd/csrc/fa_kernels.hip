@@ -10,13 +10,13 @@
 //
 // A wave holds 16*QT query rows of its candidate (a candidate's 64 queries take two waves,
 // so that everything a wave keeps stays within its share of the register file).  With v_mfma_f32_16x16x32_bf16 it forms
-// the transposed scores S^T = K Q^T (A: key rows from LDS; B: query rows in registers),
+// the transposed scores S^T = K Q^T (A: key rows, B: query rows, both read from LDS),
 // so lane (g, j) ends up with the scores of query j against keys 4g .. 4g+3 of every
 // 16-key tile.  Those are exactly the values it must supply for O^T = V^T P^T (B operand
 // P^T: query j, 8 keys), once the k slots of each 32-key step are taken as keys
 // 4g .. 4g+3 and 16+4g .. 16+4g+3: no data moves between lanes for P.  V^T's fragments
-// (A operand: one d row, the same 8 keys) are two 8-byte LDS reads, because V is written
-// into LDS transposed when it is staged.  The output O^T leaves lane (g, j) with query j,
+// (A operand: one d row, the same 8 keys) are one 16-byte LDS read, because V is transposed
+// once per user, with the keys of each 32-key group in that slot order, by the grouping launch.  The output O^T leaves lane (g, j) with query j,
 // so the running maximum, the rescaling of O and the row sums are lane-local; only the
 // block maximum is reduced across the four lane groups.  Softmax runs in base 2 (scores
 // scaled by scale * log2 e, v_exp_f32), with the running maximum subtracted.
@@ -48,6 +48,9 @@ __global__ void __launch_bounds__(kFaPrepBlock) fa_prep_kernel(FaPrepArgs a) {
     }
     // One tile of 64 keys of one (user, head): V rows into LDS (row stride hd + 2 elements),
     // then each thread gathers 8 keys of one d column and writes them as 16 bytes of Vt.
+    // Within each 32-key group, positions 8g .. 8g+7 hold keys 4g .. 4g+3 and 16+4g .. 16+4g+3:
+    // the order in which lane group g feeds keys to the matrix cores, so that a lane's V^T
+    // fragment is one 16-byte read.
     const int n_kb = (a.L_kv + kFaKeys - 1) / kFaKeys;
     const int L_pad = n_kb * kFaKeys;
     const int t = (int)blockIdx.x - 1;
@@ -65,11 +68,14 @@ __global__ void __launch_bounds__(kFaPrepBlock) fa_prep_kernel(FaPrepArgs a) {
     }
     __syncthreads();
     for (int c = (int)threadIdx.x; c < hd * (kFaKeys / 8); c += (int)blockDim.x) {
-        const int d = c / (kFaKeys / 8), k0 = 8 * (c % (kFaKeys / 8));
+        const int d = c / (kFaKeys / 8), k0 = 8 * (c % (kFaKeys / 8));   // positions k0 .. k0+7
+        const int base = (k0 & ~31) + 4 * ((k0 & 31) >> 3);              // key at position k0
         u32x4_t w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            w[e] = (uint32_t)tile[(k0 + 2 * e) * ld + d] | ((uint32_t)tile[(k0 + 2 * e + 1) * ld + d] << 16);
+        for (int e = 0; e < 4; ++e) {
+            const int ka = base + (e < 2 ? 2 * e : 16 + 2 * (e - 2));       // positions k0+2e, k0+2e+1
+            w[e] = (uint32_t)tile[ka * ld + d] | ((uint32_t)tile[(ka + 1) * ld + d] << 16);
+        }
         *reinterpret_cast<u32x4_t *>(a.Vt + ((size_t)uh * hd + d) * L_pad + kb * kFaKeys + k0) = w;
     }
 }
@@ -258,10 +264,7 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const char *row = Vl + (16 * dt + j) * L::VROW;
-                const u32x2_t v0 = *reinterpret_cast<const u32x2_t *>(row + (32 * s + 4 * g) * 2);
-                const u32x2_t v1 = *reinterpret_cast<const u32x2_t *>(row + (32 * s + 16 + 4 * g) * 2);
-                const u32x4_t vf = (u32x4_t){v0[0], v0[1], v1[0], v1[1]};
+                const u32x4_t vf = *reinterpret_cast<const u32x4_t *>(Vl + (16 * dt + j) * L::VROW + (32 * s + 8 * g) * 2);
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = mfma_bf16(vf, pf[s][qt], oacc[dt][qt]);
             }
