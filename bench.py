@@ -441,7 +441,8 @@ def run_fa(args) -> int:
         rng = np.random.default_rng(7)
         rows = [(int(b), int(rng.integers(0, c.H)), int(rng.integers(0, c.L_q))) for b in rng.integers(0, c.B_c, 64)]
         ref = oracle.fa_f64(x.Q, x.K, x.V, x.map, rows=rows)
-        nbad, _ = oracle.tolerance_violations(np.stack([On[r] for r in rows]), ref)
+        nbad, _ = oracle.tolerance_violations(np.stack([On[r] for r in rows]), ref,
+                                              extra=oracle.fa_weight_bound(x.Q, x.K, x.V, x.map, rows=rows))
         out["parity"] = {"rows_checked": len(rows), "violations": nbad}
         # The oracle on a bounded sample: query rows one by one, for about cpu_seconds.
         threads = oracle.max_threads()

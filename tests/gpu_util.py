@@ -67,9 +67,9 @@ def mismatch_pattern(Y_gpu: np.ndarray, Y_ref: np.ndarray) -> str:
             f"row blocks {np.bincount(m // 16).tolist()}, column slots {np.bincount(d // 8).tolist()}")
 
 
-def assert_close(Y_gpu: np.ndarray, Y_ref: np.ndarray, what: str):
+def assert_close(Y_gpu: np.ndarray, Y_ref: np.ndarray, what: str, extra=None):
     import oracle
-    nbad, excess = oracle.tolerance_violations(Y_gpu, Y_ref, ATOL, RTOL)
+    nbad, excess = oracle.tolerance_violations(Y_gpu, Y_ref, ATOL, RTOL, extra)
     assert nbad == 0, (f"{what}: {nbad} of {Y_ref.size} elements outside tolerance (max excess {excess:.3g})"
                        + mismatch_pattern(Y_gpu, Y_ref))
 

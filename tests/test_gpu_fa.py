@@ -4,8 +4,10 @@ O[b,h] = softmax(scale Q[b,h] K[map[b],h]^T) V[map[b],h] (IKBO recsys blog, "Dee
 Flash Attention").  Small shapes with ragged key counts, partial candidate groups, users
 without candidates and both head sizes are compared element by element; the attention
 configurations at full size on sampled query rows.  Bar, per element:
-|O - O_ref| <= 1e-3 + 1.6e-2 |O_ref| (bf16 inputs and output, fp32 accumulation, bf16
-softmax weights into the matrix cores).
+|O - O_ref| <= 1e-3 + 1.6e-2 |O_ref| + 2^-8 sum_k w_k |V_k|: the LCE bar (bf16 inputs and
+output, fp32 accumulation) plus twice what bf16 rounding of the softmax weights w (at most
+2^-9 of each weight) can move an output; the pages fix no precision for attention, and the
+last term matters only when few keys carry the weight.
 """
 import numpy as np
 import pytest
@@ -60,7 +62,7 @@ def test_fa_small_elementwise(shape):
         x.map = np.random.default_rng(3).choice(np.array([0, 2, 5], np.int32), B_c).astype(np.int32)
     O = gpu_fa(x)
     ref = oracle.fa_f64(x.Q, x.K, x.V, x.map)
-    assert_close(O, ref, f"fa {shape}")
+    assert_close(O, ref, f"fa {shape}", oracle.fa_weight_bound(x.Q, x.K, x.V, x.map))
 
 
 def _rows(cfg, mp, rng):
@@ -80,7 +82,8 @@ def test_fa_full_size_sampled(name):
     O = gpu_fa(x)
     rows = _rows(cfg, x.map, np.random.default_rng(41))
     ref = oracle.fa_f64(x.Q, x.K, x.V, x.map, rows=rows)
-    assert_close(np.stack([O[r] for r in rows]), ref, f"{name} sampled rows")
+    assert_close(np.stack([O[r] for r in rows]), ref, f"{name} sampled rows",
+                 oracle.fa_weight_bound(x.Q, x.K, x.V, x.map, rows=rows))
     assert np.all(np.isfinite(O))
 
 

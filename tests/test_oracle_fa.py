@@ -95,3 +95,16 @@ def test_fa_mutants(tmp_path, name):
     f = _build_mutant(tmp_path, name, old, new)
     failed = pins_fa.run_all(f, "bf16") + pins_fa.run_all(f, "f32")
     assert failed, f"planted slip '{name}' passed every pin"
+
+
+def test_weight_bound_is_the_attention_of_abs_v(oracle_mod):
+    """The attention bar's extra term: 2^-8 times the oracle's attention over |V|, which lies
+    between the smallest and largest |V| row value and is zero for V = 0."""
+    from broadcast_gemm_amd.inputs import FA_CONFIGS, make_fa_inputs
+    from pins import _f
+    x = make_fa_inputs(FA_CONFIGS[0])
+    wb = oracle_mod.fa_weight_bound(x.Q, x.K, x.V, x.map)
+    Va = np.abs(_f(x.V))[x.map]
+    assert np.all(wb >= Va.min(axis=2, keepdims=True) * 2.0 ** -8 - 1e-15)
+    assert np.all(wb <= Va.max(axis=2, keepdims=True) * 2.0 ** -8 + 1e-15)
+    assert np.all(oracle_mod.fa_weight_bound(x.Q, x.K, np.zeros_like(x.V), x.map) == 0)
