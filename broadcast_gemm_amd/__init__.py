@@ -42,7 +42,7 @@ FLAG_BACKWARD = 8
 
 # Every symbol include/ikbo.h declares.
 EXPORTED = ("ikbo_lce_plan", "ikbo_lce_forward", "ikbo_lce_backward", "ikbo_lce_check",
-            "ikbo_fa_plan", "ikbo_fa_forward", "ikbo_fa_check", "ikbo_fa_plan_destroy", "ikbo_lce_plan_info",
+            "ikbo_fa_plan", "ikbo_fa_forward", "ikbo_fa_forward_fused", "ikbo_fa_check", "ikbo_fa_plan_destroy", "ikbo_lce_plan_info",
             "ikbo_lce_plan_set_spin_limit", "ikbo_lce_plan_destroy", "ikbo_status_str",
             "ikbo_last_error_message")
 
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.ikbo_fa_plan.restype = ip
         L.ikbo_fa_forward.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, ctypes.c_float, vp]
         L.ikbo_fa_forward.restype = ip
+        L.ikbo_fa_forward_fused.argtypes = [vp] * 8 + [i] * 7 + [ctypes.c_float, vp]
+        L.ikbo_fa_forward_fused.restype = ip
         L.ikbo_fa_check.argtypes = [vp, vp]
         L.ikbo_fa_check.restype = ip
         L.ikbo_fa_plan_destroy.argtypes = [vp]
@@ -300,6 +302,34 @@ class FaPlan:
         if st != IKBO_OK:
             raise IkboError(st, "ikbo_fa_forward")
         return out
+
+    def forward_fused_ptrs(self, Q: int, K: int, V: int, mp: int, O: int, Q_self: int, O_self: int, B_u: int,
+                           B_c: int, L_self: int, scale: float = 0.0, stream: Optional[int] = None) -> int:
+        H, L_q, L_kv, hd = self.dims
+        return lib().ikbo_fa_forward_fused(self.handle, Q, K, V, mp, O, Q_self, O_self, B_u, B_c, H, L_q, L_kv,
+                                           L_self, hd, float(scale), stream)
+
+    def forward_fused(self, Q, K, V, mp, Q_self, out=None, out_self=None, scale: float = 0.0, stream=None):
+        """Target attention of the candidates and self-attention of the users' own queries
+        Q_self [B_u, H, L_self, hd] over the same K/V, in one launch; returns (O, O_self)."""
+        torch = _torch()
+        for name, t in (("Q", Q), ("K", K), ("V", V), ("Q_self", Q_self)):
+            if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bfloat16 tensor on the GPU")
+        mp = mp.to(torch.int32).contiguous()
+        H, L_q, L_kv, hd = self.dims
+        B_c, B_u, L_self = Q.shape[0], K.shape[0], Q_self.shape[2]
+        if tuple(Q.shape) != (B_c, H, L_q, hd) or tuple(K.shape) != (B_u, H, L_kv, hd) or K.shape != V.shape \
+                or tuple(Q_self.shape) != (B_u, H, L_self, hd) or mp.shape != (B_c,):
+            raise IkboError(IKBO_ERR_INVALID_ARG, "shape differs from the plan")
+        out = torch.empty_like(Q) if out is None else out
+        out_self = torch.empty_like(Q_self) if out_self is None else out_self
+        st = self.forward_fused_ptrs(Q.data_ptr(), K.data_ptr(), V.data_ptr(), mp.data_ptr(), out.data_ptr(),
+                                     Q_self.data_ptr(), out_self.data_ptr(), B_u, B_c, L_self, scale,
+                                     _stream_handle(stream))
+        if st != IKBO_OK:
+            raise IkboError(st, "ikbo_fa_forward_fused")
+        return out, out_self
 
     def check(self, stream=None) -> int:
         """Synchronise and return (and clear) the device-side status."""

@@ -25,6 +25,7 @@ struct FaPrepArgs {
     const uint16_t *V;            // [B_u][H][L_kv][hd]
     uint16_t *Vt;                 // [B_u][H][hd][L_kv_pad]
     int B_u, B_c, H, L_kv, hd;
+    int n_self;                   // self-attention query chunks (of L_q) per user, after its candidates
 };
 size_t fa_prep_lds_bytes(int B_u, int B_c, int hd);
 hipError_t launch_fa_prep(const FaPrepArgs &a, hipStream_t s);
@@ -34,8 +35,11 @@ struct FaArgs {
     const uint16_t *K;            // [B_u][H][L_kv][hd]
     const uint16_t *Vt;           // [B_u][H][hd][L_kv_pad]
     uint16_t *O;                  // [B_c][H][L_q][hd]
+    const uint16_t *Q_self;       // [B_u][H][n_self * L_q][hd] (null when n_self = 0)
+    uint16_t *O_self;             // same shape as Q_self
     const int32_t *perm, *off, *goff;
     int B_u, H, L_q, L_kv, hd;
+    int n_self;
     int n_groups_max;             // blocks per head in the grid (>= goff[B_u])
     float scale_log2;             // softmax scale times log2(e)
 };

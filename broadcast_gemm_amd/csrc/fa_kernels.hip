@@ -6,7 +6,10 @@
 // user share one copy, and a block computes up to kFaGroup of them (one wave each) for one
 // head, so every K/V block it stages in LDS serves all of them.  Blocks are launched with
 // the candidate groups before the heads, so that the blocks running together read the
-// same user's K/V (the pages' grid order for L2 reuse).
+// same user's K/V (the pages' grid order for L2 reuse).  Self-attention of the user's own
+// sequence (queries from the user side over the same K/V) rides in the same launch: its
+// query chunks are further work slots of the user, after the candidates, so they share the
+// staged K/V blocks as well (the pages' self + target attention fusion).
 //
 // A wave holds 16*QT query rows of its candidate (a candidate's 64 queries take two waves,
 // so that everything a wave keeps stays within its share of the register file).  With v_mfma_f32_16x16x32_bf16 it forms
@@ -40,7 +43,7 @@ __global__ void __launch_bounds__(kFaPrepBlock) fa_prep_kernel(FaPrepArgs a) {
             int run = 0;
             for (int u = 0; u < a.B_u; ++u) {
                 a.goff[u] = run;
-                run += (offs[u + 1] - offs[u] + kFaGroup - 1) / kFaGroup;
+                run += (offs[u + 1] - offs[u] + a.n_self + kFaGroup - 1) / kFaGroup;
             }
             a.goff[a.B_u] = run;
         }
@@ -125,10 +128,18 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
         else hi = mid;
     }
     const int u = lo;
-    const int first = a.off[u] + (gi - a.goff[u]) * kFaGroup;
-    const int cs = wv / WPC, q0 = 16 * QT * (wv % WPC);   // candidate slot, first query row
-    const bool active = first + cs < a.off[u + 1];
-    const int b = active ? a.perm[first + cs] : 0;
+    // Work slots of user u: its candidates (in user order), then its n_self chunks of L_q
+    // self-attention queries; a block takes kFaGroup consecutive slots, one per candidate slot cs.
+    const int cs = wv / WPC, q0 = 16 * QT * (wv % WPC);   // slot in the block, first query row
+    const int slot = (gi - a.goff[u]) * kFaGroup + cs;
+    const int n_cand = a.off[u + 1] - a.off[u];
+    const bool is_cand = slot < n_cand;
+    const bool active = slot < n_cand + a.n_self;
+    const size_t qbase = !active  ? 0
+                         : is_cand ? ((size_t)a.perm[a.off[u] + slot] * a.H + h) * a.L_q * HD
+                                   : (((size_t)u * a.H + h) * a.n_self + (slot - n_cand)) * a.L_q * HD;
+    const uint16_t *Qsrc = is_cand ? a.Q : a.Q_self;
+    uint16_t *Odst = is_cand ? a.O : a.O_self;
 
     const size_t kv0 = ((size_t)u * a.H + h) * a.L_kv * HD;
     const __amdgpu_buffer_rsrc_t rsK = uniform_rsrc(a.K + kv0, a.L_kv * HD * 2);
@@ -137,8 +148,7 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
     // 16*qt + j, d = 32t + 8g .. +7); a wave reads only what it wrote, so no barrier is needed.
     char *Ql = lds + 2 * L::BUF + wv * L::QWAVE;
     {
-        const __amdgpu_buffer_rsrc_t rsQ =
-            uniform_rsrc(active ? a.Q + ((size_t)b * a.H + h) * a.L_q * HD : nullptr, active ? a.L_q * HD * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rsQ = uniform_rsrc(active ? Qsrc + qbase : nullptr, active ? a.L_q * HD * 2 : 0);
         constexpr int PER = 16 * QT * HD / 8 / 64;   // 16-byte chunks per lane
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -302,7 +312,7 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
     }
     if (!active) return;
     // O[b, h, 16*qt + j, 16*dt + 4g .. +3] = O^T / row sum.
-    uint16_t *ob = a.O + ((size_t)b * a.H + h) * a.L_q * HD;
+    uint16_t *ob = Odst + qbase;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         const float inv = 1.0f / wave_sum4(l[qt]);

@@ -78,16 +78,23 @@ int ikbo_fa_plan(ikbo_fa_plan_t *out, int max_B_u, int max_B_c, int H, int L_q, 
     return IKBO_OK;
 }
 
-int ikbo_fa_forward(ikbo_fa_plan_t p, const void *Q, const void *K, const void *V, const int32_t *map, void *O,
-                    int B_u, int B_c, int H, int L_q, int L_kv, int head_dim, float scale, void *stream) {
+int ikbo_fa_forward_fused(ikbo_fa_plan_t p, const void *Q, const void *K, const void *V, const int32_t *map,
+                          void *O, const void *Q_self, void *O_self, int B_u, int B_c, int H, int L_q, int L_kv,
+                          int L_self, int head_dim, float scale, void *stream) {
     if (p == nullptr) return IKBO_ERR_INVALID_ARG;
     if (H != p->H || L_q != p->L_q || L_kv != p->L_kv || head_dim != p->hd) return IKBO_ERR_INVALID_ARG;
     if (B_c < 0 || B_c > p->max_B_c || B_u < 1 || B_u > p->max_B_u) return IKBO_ERR_INVALID_ARG;
+    if (L_self < 0 || L_self % L_q != 0 || (long long)L_self * head_dim * 2 >= (1LL << 31)) return IKBO_ERR_INVALID_ARG;
     if (!(scale >= 0.0f) || std::isinf(scale)) return IKBO_ERR_INVALID_ARG;
-    if (B_c == 0) return IKBO_OK;
-    if (!Q || !K || !V || !map || !O) return IKBO_ERR_INVALID_ARG;
-    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || (reinterpret_cast<uintptr_t>(map) & 3u))
+    if (B_c == 0 && L_self == 0) return IKBO_OK;
+    if (!K || !V || (B_c > 0 && (!Q || !map || !O)) || (L_self > 0 && (!Q_self || !O_self))) return IKBO_ERR_INVALID_ARG;
+    if (!aligned16(K) || !aligned16(V) || (B_c > 0 && (!aligned16(Q) || !aligned16(O) ||
+                                                       (reinterpret_cast<uintptr_t>(map) & 3u))) ||
+        (L_self > 0 && (!aligned16(Q_self) || !aligned16(O_self))))
         return IKBO_ERR_ALIGNMENT;
+    const int n_self = L_self / L_q;
+    if ((long long)((B_c + (long long)B_u * n_self + kFaGroup - 1) / kFaGroup + B_u) * H >= (1LL << 31))
+        return IKBO_ERR_UNSUPPORTED;
     int cur = -1;
     hipError_t e = hipGetDevice(&cur);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -96,18 +103,29 @@ int ikbo_fa_forward(ikbo_fa_plan_t p, const void *Q, const void *K, const void *
     FaPrepArgs pa{};
     pa.map = map; pa.perm = p->perm; pa.off = p->off; pa.goff = p->goff; pa.err = p->err;
     pa.V = static_cast<const uint16_t *>(V); pa.Vt = p->Vt;
-    pa.B_u = B_u; pa.B_c = B_c; pa.H = H; pa.L_kv = L_kv; pa.hd = head_dim;
+    pa.B_u = B_u; pa.B_c = B_c; pa.H = H; pa.L_kv = L_kv; pa.hd = head_dim; pa.n_self = n_self;
     if ((e = launch_fa_prep(pa, s)) != hipSuccess) return hip_fail(e, "fa prep");
     FaArgs a{};
     a.Q = static_cast<const uint16_t *>(Q); a.K = static_cast<const uint16_t *>(K);
     a.Vt = p->Vt; a.O = static_cast<uint16_t *>(O);
+    a.Q_self = static_cast<const uint16_t *>(Q_self); a.O_self = static_cast<uint16_t *>(O_self);
     a.perm = p->perm; a.off = p->off; a.goff = p->goff;
-    a.B_u = B_u; a.H = H; a.L_q = L_q; a.L_kv = L_kv; a.hd = head_dim;
-    a.n_groups_max = (B_c + kFaGroup - 1) / kFaGroup + B_u;
+    a.B_u = B_u; a.H = H; a.L_q = L_q; a.L_kv = L_kv; a.hd = head_dim; a.n_self = n_self;
+    a.n_groups_max = (int)((B_c + (long long)B_u * n_self + kFaGroup - 1) / kFaGroup + B_u);
     const float sc = scale > 0.0f ? scale : 1.0f / std::sqrt((float)head_dim);
     a.scale_log2 = sc * 1.4426950408889634f;
     if ((e = launch_fa_forward(a, s)) != hipSuccess) return hip_fail(e, "fa forward");
     return IKBO_OK;
+}
+
+int ikbo_fa_forward(ikbo_fa_plan_t p, const void *Q, const void *K, const void *V, const int32_t *map, void *O,
+                    int B_u, int B_c, int H, int L_q, int L_kv, int head_dim, float scale, void *stream) {
+    if (p == nullptr) return IKBO_ERR_INVALID_ARG;
+    if (B_c == 0 && B_u >= 1 && B_u <= p->max_B_u && H == p->H && L_q == p->L_q && L_kv == p->L_kv &&
+        head_dim == p->hd && scale >= 0.0f && !std::isinf(scale))
+        return IKBO_OK;
+    return ikbo_fa_forward_fused(p, Q, K, V, map, O, nullptr, nullptr, B_u, B_c, H, L_q, L_kv, 0, head_dim, scale,
+                                 stream);
 }
 
 int ikbo_fa_check(ikbo_fa_plan_t p, void *stream) {

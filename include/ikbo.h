@@ -203,6 +203,23 @@ int ikbo_fa_forward(ikbo_fa_plan_t plan, const void *Q, const void *K, const voi
                     void *O, int B_u, int B_c, int H, int L_q, int L_kv, int head_dim, float scale,
                     void *stream);
 
+/*
+ * Self + target attention in one launch (blog, "Self + Target Attention Fusion"): besides the
+ * candidates' target attention above, the user sequence's own queries attend over the same K
+ * and V (no mask, like the target queries):
+ *
+ *     O_self[u,h] = softmax(scale * Q_self[u,h] . K[u,h]^T) . V[u,h]        for u < B_u
+ *
+ * Q_self, O_self [B_u, H, L_self, head_dim] bf16 (16-byte aligned); L_self a multiple of L_q
+ * (the self queries are taken L_q at a time, as further work of their user, so they share the
+ * K/V blocks the user's candidates stage).  L_self = 0 is ikbo_fa_forward; B_c = 0 computes
+ * only the self part (Q, map and O may then be NULL).  Otherwise as ikbo_fa_forward.
+ */
+int ikbo_fa_forward_fused(ikbo_fa_plan_t plan, const void *Q, const void *K, const void *V,
+                          const int32_t *map, void *O, const void *Q_self, void *O_self, int B_u,
+                          int B_c, int H, int L_q, int L_kv, int L_self, int head_dim, float scale,
+                          void *stream);
+
 /* Wait for `stream`, then return and clear the device status (IKBO_OK or IKBO_ERR_MAP_RANGE). */
 int ikbo_fa_check(ikbo_fa_plan_t plan, void *stream);
 
