@@ -464,6 +464,83 @@ def run_fa(args) -> int:
     return 0
 
 
+def run_fa_fused(args) -> int:
+    """Self + target attention at fa-70to1 with the users' 1024-token sequences as self
+    queries: one fused launch against a target launch followed by a self launch."""
+    import numpy as np
+    import torch
+
+    import broadcast_gemm_amd as bga
+    from broadcast_gemm_amd.inputs import FA_CONFIG_BY_NAME, f32_to_bf16_bits, make_fa_inputs
+
+    c = FA_CONFIG_BY_NAME["fa-70to1"]
+    L_self = c.L_kv
+    torch.cuda.set_device(0)
+    x = make_fa_inputs(c)
+    Qs = f32_to_bf16_bits(np.random.default_rng(c.seed + 500).standard_normal((c.B_u, c.H, L_self, c.hd),
+                                                                              dtype=np.float32))
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    base = [dev(a) for a in (x.Q, x.K, x.V, x.map, Qs)]
+    set_bytes = sum(t.numel() * t.element_size() for t in base) * 2
+    n_sets = max(1, math.ceil(args.rotate_mb * 2**20 / set_bytes))
+    sets = [(base if i == 0 else [t.clone() for t in base]) + [torch.empty_like(base[0]), torch.empty_like(base[4])]
+            for i in range(n_sets)]
+    plan = bga.FaPlan(c.B_u, c.B_c, c.H, c.L_q, c.L_kv, c.hd)
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def fused(i):
+        Q, K, V, mp, Q_s, O, O_s = sets[i % n_sets]
+        st = plan.forward_fused_ptrs(Q.data_ptr(), K.data_ptr(), V.data_ptr(), mp.data_ptr(), O.data_ptr(),
+                                     Q_s.data_ptr(), O_s.data_ptr(), c.B_u, c.B_c, L_self, 0.0, sh)
+        assert st == bga.IKBO_OK, bga.status_str(st)
+
+    def separate(i):
+        Q, K, V, mp, Q_s, O, O_s = sets[i % n_sets]
+        st = plan.forward_ptrs(Q.data_ptr(), K.data_ptr(), V.data_ptr(), mp.data_ptr(), O.data_ptr(), c.B_u, c.B_c,
+                               0.0, sh)
+        assert st == bga.IKBO_OK, bga.status_str(st)
+        st = plan.forward_fused_ptrs(0, K.data_ptr(), V.data_ptr(), 0, 0, Q_s.data_ptr(), O_s.data_ptr(), c.B_u, 0,
+                                     L_self, 0.0, sh)
+        assert st == bga.IKBO_OK, bga.status_str(st)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(args.steps):
+            fn(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    ms_sep = timed(separate)
+    ms_fused = timed(fused)
+    assert plan.check() == bga.IKBO_OK
+    flops = fa_flops(c) + 4 * c.B_u * c.H * L_self * c.L_kv * c.hd
+    tf = flops / (ms_fused * 1e-3) / 1e12
+    out = {"metric": "IKBO self + target attention TFLOP/s, fa-70to1 with 1024 self queries per user",
+           "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_fused, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": c.dtype, "data": "synthetic",
+           "config": {"workload": c.name + "+self1024", "L_self": L_self, "rotating_sets": n_sets,
+                      "parallelism": "single GPU"},
+           "us_fused": round(ms_fused * 1e3, 3), "us_separate_two_launches": round(ms_sep * 1e3, 3),
+           "speedup_fused_over_separate": round(ms_sep / ms_fused, 4), "algorithmic_flops": flops,
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "kernel": "fa_fwd_kernel, fused (plus the grouping launch)"}}
+    plan.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def run_copy(args) -> int:
     """Plain device copy of known size (calibrates FETCH_SIZE/WRITE_SIZE counters)."""
     import torch
@@ -487,7 +564,7 @@ def main() -> int:
     ap.add_argument("--rotate-mb", type=int, default=1100, help="total size of rotated buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--mode", default="lce", choices=["lce", "copy", "traffic", "rewrite", "backward", "fa"])
+    ap.add_argument("--mode", default="lce", choices=["lce", "copy", "traffic", "rewrite", "backward", "fa", "fa-fused"])
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="--mode traffic: rocprofv3 --pmc output directories")
@@ -511,6 +588,8 @@ def main() -> int:
         return run_copy(args)
     if args.mode == "fa":
         return run_fa(args)
+    if args.mode == "fa-fused":
+        return run_fa_fused(args)
 
     import broadcast_gemm_amd as bga
     from broadcast_gemm_amd.inputs import CONFIG_BY_NAME, bf16_bits_to_f32, make_inputs
