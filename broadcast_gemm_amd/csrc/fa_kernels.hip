@@ -85,12 +85,12 @@ __global__ void __launch_bounds__(kFaPrepBlock) fa_prep_kernel(FaPrepArgs a) {
 
 template <int HD, int NT>
 struct FaLds {
-    static constexpr int KROW = HD * 2 + 16;        // bytes per staged K row (padded)
+    static constexpr int KROW = HD * 2 + 32;        // bytes per staged K row (padded: fewer LDS bank conflicts than 16)
     static constexpr int VROW = kFaKeys * 2 + 16;   // bytes per staged V^T row (padded)
     static constexpr int KBYTES = kFaKeys * KROW;
     static constexpr int BUF = KBYTES + HD * VROW;  // one K block and one V^T block
     static constexpr int CHUNKS = kFaKeys * HD / 8 / NT;   // 16-byte chunks per thread per block (NT threads)
-    static constexpr int QROW = HD * 2 + 16;        // bytes per staged query row (padded)
+    static constexpr int QROW = HD * 2 + 32;        // bytes per staged query row (padded likewise)
     static constexpr int QWAVE = 64 * QROW / (NT / 64 / kFaGroup);   // one wave's query rows (64/WPC of them)
     static constexpr int TOTAL = 2 * BUF + (NT / 64) * QWAVE;
 };
