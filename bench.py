@@ -220,6 +220,75 @@ def run_rewrite(args, cfg, sets) -> int:
     return 0 if st == 0 else 1
 
 
+def run_rewrite_fa(args) -> int:
+    """An unmodified model's target attention over a materialised broadcast (K[map], V[map],
+    then torch's fused attention on the GPU) against the same module after the inference-time
+    rewrite (broadcast_gemm_amd.rewrite.rewrite_attention), on rotated input sets.  torch's
+    attention is held to its fused backends; where none serves the shape the line says so."""
+    import numpy as np
+    import torch
+    import torch.fx as fx
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    from broadcast_gemm_amd import rewrite as rw
+    from broadcast_gemm_amd.inputs import FA_CONFIG_BY_NAME, make_fa_inputs
+
+    name = args.config if args.config in FA_CONFIG_BY_NAME else "fa-70to1"
+    c = FA_CONFIG_BY_NAME[name]
+    torch.cuda.set_device(0)
+    print(f"[bench] attention rewrite config={c.name} steps={args.steps} warmup={args.warmup}", file=sys.stderr,
+          flush=True)
+    x = make_fa_inputs(c)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    base = [dev(a) for a in (x.Q, x.K, x.V)] + [dev(x.map).long()]
+    set_bytes = sum(t.numel() * t.element_size() for t in base)
+    n_sets = max(1, math.ceil(args.rotate_mb * 2**20 / set_bytes))
+    sets = [base if i == 0 else [t.clone() for t in base] for i in range(n_sets)]
+
+    class Materialised(torch.nn.Module):
+        def forward(self, Q, K, V, mp):
+            return F.scaled_dot_product_attention(Q, K[mp], V[mp])
+
+    model = Materialised()
+    gm = fx.symbolic_trace(model)
+    assert rw.rewrite_attention(gm, *sets[0]) == 1
+
+    def timed(fn):
+        with torch.no_grad():
+            for i in range(args.warmup):
+                fn(*sets[i % n_sets])
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(args.steps):
+                fn(*sets[i % n_sets])
+            e1.record()
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / args.steps
+
+    t_rw = timed(gm)
+    st = rw.fa_plan_table().check_all()
+    t_mat, why = None, None
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            t_mat = timed(model)
+    except RuntimeError as e:
+        why = str(e).splitlines()[0][:160]
+    out = {"mode": "rewrite-fa", "config": c.name, "steps": args.steps, "warmup": args.warmup,
+           "materialised_torch_us": None if t_mat is None else round(t_mat, 3),
+           "rewritten_ikbo_us": round(t_rw, 3),
+           "speedup": None if t_mat is None else round(t_mat / t_rw, 2),
+           "torch_unavailable": why, "device_status": st, "rotating_sets": n_sets}
+    print(json.dumps(out), flush=True)
+    return 0 if st == 0 else 1
+
+
 def backward_bytes(cfg) -> int:
     """Algorithmic HBM bytes of one backward: dY, C, U, W_u, W_c and map read once; dC, dU
     (input dtype) and dW_u, dW_c (fp32) written once."""
@@ -564,7 +633,7 @@ def main() -> int:
     ap.add_argument("--rotate-mb", type=int, default=1100, help="total size of rotated buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--mode", default="lce", choices=["lce", "copy", "traffic", "rewrite", "backward", "fa", "fa-fused"])
+    ap.add_argument("--mode", default="lce", choices=["lce", "copy", "traffic", "rewrite", "rewrite-fa", "backward", "fa", "fa-fused"])
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="--mode traffic: rocprofv3 --pmc output directories")
@@ -588,6 +657,8 @@ def main() -> int:
         return run_copy(args)
     if args.mode == "fa":
         return run_fa(args)
+    if args.mode == "rewrite-fa":
+        return run_rewrite_fa(args)
     if args.mode == "fa-fused":
         return run_fa_fused(args)
 

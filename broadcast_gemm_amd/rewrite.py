@@ -6,7 +6,7 @@ the model (IKBO recsys blog, the section on how the IKBO co-design is built and 
 FAQ; aibriefing article, the paragraph on the three layers of the stack).  The same
 passages say the compiler needs each operator's dynamic shape range to pick the kernel.
 
-This module is that pass for torch.fx graphs.  It finds
+This module is that pass for torch.fx graphs, for the pages' two kernels.  For the LCE it finds
 
     X = cat([U[map], C], dim=1)        (U[map] as indexing or index_select along dim 0;
     Y = W @ X                           the blocks in either order; @ as matmul, or bmm
@@ -19,6 +19,16 @@ a plan from ``PlanTable``, which sizes plans by shape range: candidate batches a
 up to the pages' 256..4096 range (then to multiples of 4096), user batches to powers of
 two, and a plan is replaced by a larger one when a call outgrows it.
 
+For target attention (IKBO recsys blog, "Deep Dive: Flash Attention") it finds
+
+    O = scaled_dot_product_attention(Q, K[map], V[map])   (K and V gathered by the same index,
+                                                           no mask, no dropout, not causal)
+
+with bf16 Q [B_c, H, L_q, hd] and K, V [B_u, H, L_kv, hd] in the shapes the library serves
+(hd 64 or 128, L_q 16, 32 or 64), and replaces O by ``ikbo_target_attention(Q, K, V, map,
+scale)``, which never replicates K and V; plans come from ``FaPlanTable``, sized by the same
+batch ranges.
+
 Only the graph is rewritten; every forward runs in the HIP library (no CPU fallback).
 """
 from __future__ import annotations
@@ -26,7 +36,7 @@ from __future__ import annotations
 import operator
 from typing import Dict, Optional, Tuple
 
-from . import LcePlan
+from . import FaPlan, LcePlan
 
 B_C_BUCKETS = (256, 512, 1024, 2048, 4096)   # candidate batch range (the pages' practical advice)
 
@@ -97,6 +107,56 @@ def ikbo_lce(U, C, mp, W_u, W_c):
     B_c, K_c, _ = C.shape
     plan = plan_table().plan_for(B_u, B_c, K_u, K_c, W_u.shape[0], D, dtype)
     return plan.forward(U.contiguous(), C.contiguous(), mp, W_u.contiguous(), W_c.contiguous())
+
+
+class FaPlanTable:
+    """Attention plans keyed by (H, L_q, L_kv, head_dim), each sized to a batch range."""
+
+    def __init__(self, make_plan=FaPlan):
+        self._make = make_plan
+        self._plans: Dict[Tuple, object] = {}
+
+    def plan_for(self, B_u: int, B_c: int, H: int, L_q: int, L_kv: int, hd: int):
+        key = (H, L_q, L_kv, hd)
+        plan = self._plans.get(key)
+        if plan is None or plan.max_B_u < B_u or plan.max_B_c < B_c:
+            mu, mc = bucket_b_u(B_u), bucket_b_c(B_c)
+            if plan is not None:
+                mu, mc = max(mu, plan.max_B_u), max(mc, plan.max_B_c)
+                plan.close()
+            plan = self._make(mu, mc, H, L_q, L_kv, hd)
+            self._plans[key] = plan
+        return plan
+
+    def check_all(self) -> int:
+        for plan in self._plans.values():
+            st = plan.check()
+            if st != 0:
+                return st
+        return 0
+
+    def close(self) -> None:
+        for plan in self._plans.values():
+            plan.close()
+        self._plans.clear()
+
+
+_FA_TABLE: Optional[FaPlanTable] = None
+
+
+def fa_plan_table() -> FaPlanTable:
+    global _FA_TABLE
+    if _FA_TABLE is None:
+        _FA_TABLE = FaPlanTable()
+    return _FA_TABLE
+
+
+def ikbo_target_attention(Q, K, V, mp, scale=None):
+    """softmax(scale Q K[map]^T) V[map] per head through the plan table (the rewritten graph's call)."""
+    B_c, H, L_q, hd = Q.shape
+    B_u, _, L_kv, _ = K.shape
+    plan = fa_plan_table().plan_for(B_u, B_c, H, L_q, L_kv, hd)
+    return plan.forward(Q.contiguous(), K.contiguous(), V.contiguous(), mp, scale=0.0 if scale is None else scale)
 
 
 # ---- pattern matching on an fx graph --------------------------------------------------
@@ -205,3 +265,59 @@ def rewrite_lce(gm, *example_inputs) -> int:
         gm.graph.lint()
         gm.recompile()
     return count
+
+
+def _sdpa_args(node):
+    """(Q, K, V, scale) of an unmasked, non-causal, dropout-free SDPA call, else None."""
+    import torch.nn.functional as F
+    if not _is_call(node, (F.scaled_dot_product_attention,)):
+        return None
+    names = ["query", "key", "value", "attn_mask", "dropout_p", "is_causal", "scale"]
+    got = dict(zip(names, node.args))
+    got.update(node.kwargs)
+    if got.get("attn_mask") is not None or got.get("dropout_p", 0.0) not in (0, 0.0) or got.get("is_causal", False):
+        return None
+    if any(k not in names for k in node.kwargs):   # enable_gqa and the like: leave alone
+        return None
+    scale = got.get("scale")
+    if scale is not None and not (isinstance(scale, (int, float)) and 0 < scale < float("inf")):
+        return None                                    # the library reads 0 as 1/sqrt(head_dim)
+    return got["query"], got["key"], got["value"], scale
+
+
+def rewrite_attention(gm, *example_inputs) -> int:
+    """Replace every target attention over a gathered (broadcast) K/V in gm by
+    ikbo_target_attention.  Returns the number of rewrites; gm is recompiled in place."""
+    import torch
+    from torch.fx.passes.shape_prop import ShapeProp
+
+    ShapeProp(gm).propagate(*example_inputs)
+    count = 0
+    for node in list(gm.graph.nodes):
+        got = _sdpa_args(node)
+        if got is None:
+            continue
+        q, k, v, scale = got
+        gk, gv = (_gather_of(x) if hasattr(x, "op") else None for x in (k, v))
+        if gk is None or gv is None or gk[1] is not gv[1]:
+            continue                                   # K and V gathered by one index
+        (K, mp), (V, _) = gk, gv
+        tq, tk, tv = (x.meta.get("tensor_meta") for x in (q, K, V))
+        if tq is None or tk is None or tv is None:
+            continue
+        sq, sk = tuple(tq.shape), tuple(tk.shape)
+        if (len(sq) != 4 or len(sk) != 4 or tuple(tv.shape) != sk or sq[1] != sk[1] or sq[3] != sk[3]
+                or any(t.dtype != torch.bfloat16 for t in (tq, tk, tv))
+                or sq[3] not in (64, 128) or sq[2] not in (16, 32, 64)):
+            continue
+        with gm.graph.inserting_before(node):
+            new = gm.graph.call_function(ikbo_target_attention, (q, K, V, mp, scale))
+        node.replace_all_uses_with(new)
+        gm.graph.erase_node(node)
+        count += 1
+    if count:
+        gm.graph.eliminate_dead_code()
+        gm.graph.lint()
+        gm.recompile()
+    return count
+
