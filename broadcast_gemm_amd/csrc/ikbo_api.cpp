@@ -670,6 +670,7 @@ int ikbo_lce_backward(ikbo_lce_plan_t p, const void *dY, const void *U, const vo
         c.n_ks_u = 0; c.n_ks_c = ceil_div(M, 32);
         c.n_mchunks = p->dc_nmc; c.n_mblocks = ceil_div(K_c, 16);
         c.n_user = 0; c.n_cand = B_c * p->dc_nmc;
+        c.xcd_order = env_int("IKBO_BWD_DC_XCD", 1) != 0;   // a candidate's dc_nmc units share one L2
         c.spin_limit = p->spin_limit;
         const int grid = std::max(1, std::min(p->n_cu * p->dc_bpc, ceil_div(c.n_cand, kRowsBlock / 64)));
         if (rows_lds_bytes(c) > (size_t)p->max_lds) return IKBO_ERR_UNSUPPORTED;

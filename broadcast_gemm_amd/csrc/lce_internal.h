@@ -128,6 +128,7 @@ struct RowArgs {
     int n_user, n_cand;           // work units in this launch
     int wait_flags;               // users publish and candidates wait (users in the same launch)
     int lds_shared;               // W_u and W_c take turns in one LDS region (both do not fit at once)
+    int xcd_order;                // number blocks XCD by XCD (see lce_rows.hip)
     uint32_t spin_limit;
     uint32_t debug_flags;
 };

@@ -256,7 +256,15 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     const int g = lane >> 4, j = lane & 15;
     const int n_mc = a.n_mchunks;
     const int n_waves = (int)gridDim.x * wpb;
-    const int first = (int)__builtin_amdgcn_readfirstlane(blockIdx.x * wpb + (threadIdx.x >> 6));
+    // Workgroups run on XCD blockIdx % 8.  With xcd_order, the schedule's block numbers run XCD
+    // by XCD instead (consecutive numbers on one XCD, a bijection for any grid size), so that
+    // the several units of one batch entry, which sit on consecutive waves, share one L2.
+    int bid = (int)blockIdx.x;
+    if (a.xcd_order) {
+        const int nb = (int)gridDim.x, x = bid & 7, q = nb >> 3, r = nb & 7;
+        bid = x * q + imin_t(x, r) + (bid >> 3);
+    }
+    const int first = (int)__builtin_amdgcn_readfirstlane(bid * wpb + (threadIdx.x >> 6));
     const int D = Tile::DCOV;
 
     // ---- schedule (static, every value wave-uniform) ----
@@ -314,7 +322,7 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     extern __shared__ __align__(16) uint16_t lds[];
     uint16_t *wl_c = lds;
     uint16_t *wl_u = lds + (a.n_cand > 0 && !shared ? lds_w_elems(a.M, a.K_wc) : 0);
-    const bool need_u = (int)blockIdx.x * wpb < a.n_user;   // this block holds user units
+    const bool need_u = bid * wpb < a.n_user;   // this block holds user units
     // Batches: 15 blocks of 16 bytes per thread cover W_u of 96 x 301 and 10 cover W_c of
     // 96 x 197; with the opening steps that makes at most 63 loads per wave in flight.
     T.prologue_first(rs);
