@@ -13,6 +13,9 @@ if the library is not built, every call raises.
     plan = LcePlan(..., flags=FLAG_BACKWARD)     # the backward's workspace as well
     dU, dC, dW_u, dW_c = plan.backward(dY, U, C, map, W_u, W_c)
 
+    from broadcast_gemm_amd.autograd import IkboLce   # training: autograd over both calls
+    Y = IkboLce(K_u, K_c, M, D).cuda()(U, C, map); Y.backward(dY)
+
     fa = FaPlan(max_B_u, max_B_c, H, L_q, L_kv, head_dim)   # IKBO target attention
     O = fa.forward(Q, K, V, map)
 """
