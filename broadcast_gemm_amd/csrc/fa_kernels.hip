@@ -83,13 +83,22 @@ __global__ void __launch_bounds__(kFaPrepBlock) fa_prep_kernel(FaPrepArgs a) {
     }
 }
 
+// Staged K and V^T blocks are unpadded, with the 16-byte chunks of each row permuted by an XOR
+// with the row index (chunk c of row r sits at position c ^ (r mod chunks per row)), so that the
+// 16 rows one fragment read touches fall on different LDS banks.  They are filled by loads that
+// write LDS directly (lane i of an instruction lands at its base + 16 i, whatever it reads), each
+// lane reading the chunk that belongs at its position.
 template <int HD, int NT>
 struct FaLds {
-    static constexpr int KROW = HD * 2 + 32;        // bytes per staged K row (padded: fewer LDS bank conflicts than 16)
-    static constexpr int VROW = kFaKeys * 2 + 16;   // bytes per staged V^T row (padded)
+    static constexpr int KROW = HD * 2;             // bytes per staged K row
+    static constexpr int KCH = HD / 8;              // 16-byte chunks per K row
+    static constexpr int VROW = kFaKeys * 2;        // bytes per staged V^T row
+    static constexpr int VCH = kFaKeys / 8;         // 16-byte chunks per V^T row
     static constexpr int KBYTES = kFaKeys * KROW;
     static constexpr int BUF = KBYTES + HD * VROW;  // one K block and one V^T block
     static constexpr int CHUNKS = kFaKeys * HD / 8 / NT;   // 16-byte chunks per thread per block (NT threads)
+    static __device__ __forceinline__ int kpos(int r, int c) { return r * KROW + ((c ^ (r & (KCH - 1))) << 4); }
+    static __device__ __forceinline__ int vpos(int r, int c) { return r * VROW + ((c ^ (r & (VCH - 1))) << 4); }
     static constexpr int QROW = HD * 2 + 32;        // bytes per staged query row (padded likewise)
     static constexpr int QWAVE = 64 * QROW / (NT / 64 / kFaGroup);   // one wave's query rows (64/WPC of them)
     static constexpr int TOTAL = 2 * BUF + (NT / 64) * QWAVE;
@@ -159,31 +168,27 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
         }
     }
 
-    // Staging: K chunk c is key c / (HD/8), columns 8 * (c % (HD/8)) .. +7; V^T chunk c is
-    // d row c / 8, keys 8 * (c % 8) .. +7 of the block.
+    // Staging: wave wv's instruction i fills positions (wv * CHUNKS + i) * 64 + lane of the
+    // block's K chunks (row P / KCH, position P % KCH) and likewise of its V^T chunks (d row
+    // P / VCH); the lane reads the chunk that its position holds.  Keys past L_kv read as zero.
     const int L_pad = ((a.L_kv + kFaKeys - 1) / kFaKeys) * kFaKeys;
     const __amdgpu_buffer_rsrc_t rsV = uniform_rsrc(a.Vt + ((size_t)u * a.H + h) * HD * L_pad, HD * L_pad * 2);
-    u32x4_t kst[L::CHUNKS], vst[L::CHUNKS];
-    auto load_block = [&](int kb) {
-#pragma unroll
-        for (int i = 0; i < L::CHUNKS; ++i) {
-            const int c = tid + NT * i;
-            kst[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rsK, ((kb * kFaKeys + c / (HD / 8)) * HD + 8 * (c % (HD / 8))) * 2, 0, 0));
-            vst[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rsV, ((c / 8) * L_pad + kb * kFaKeys + 8 * (c % 8)) * 2, 0, 0));
-        }
-    };
-    auto store_block = [&](int buf) {
+    auto load_block = [&](int kb, int buf) {
         char *Kl = lds + buf * L::BUF;
         char *Vl = Kl + L::KBYTES;
 #pragma unroll
         for (int i = 0; i < L::CHUNKS; ++i) {
-            const int c = tid + NT * i;
-            *reinterpret_cast<u32x4_t *>(Kl + (c / (HD / 8)) * L::KROW + 16 * (c % (HD / 8))) = kst[i];
-            *reinterpret_cast<u32x4_t *>(Vl + (c / 8) * L::VROW + 16 * (c % 8)) = vst[i];
+            const int P0 = (wv * L::CHUNKS + i) * 64, P = P0 + lane;
+            const int kr = P / L::KCH, kc = (P % L::KCH) ^ (kr & (L::KCH - 1));
+            const int vr = P / L::VCH, vc = (P % L::VCH) ^ (vr & (L::VCH - 1));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (__attribute__((address_space(3))) void *)(Kl + 16 * P0), 16,
+                                                     ((kb * kFaKeys + kr) * HD + 8 * kc) * 2, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (__attribute__((address_space(3))) void *)(Vl + 16 * P0), 16,
+                                                     (vr * L_pad + kb * kFaKeys + 8 * vc) * 2, 0, 0, 0);
         }
     };
+    // This wave's staging loads have landed in LDS (the barrier that follows publishes them).
+    auto staged = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
     f32x4_t oacc[DT][QT];
 #pragma unroll
@@ -218,7 +223,7 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
                 qf[qt] = *reinterpret_cast<const u32x4_t *>(Ql + (16 * qt + j) * L::QROW + (32 * t + 8 * g) * 2);
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
-                const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(Kl + (16 * kt + j) * L::KROW + (32 * t + 8 * g) * 2);
+                const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(Kl + L::kpos(16 * kt + j, 4 * t + g));
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt) st[kt][qt] = mfma_bf16(kf, qf[qt], st[kt][qt]);
             }
@@ -274,7 +279,7 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const u32x4_t vf = *reinterpret_cast<const u32x4_t *>(Vl + (16 * dt + j) * L::VROW + (32 * s + 8 * g) * 2);
+                const u32x4_t vf = *reinterpret_cast<const u32x4_t *>(Vl + L::vpos(16 * dt + j, 4 * s + g));
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = mfma_bf16(vf, pf[s][qt], oacc[dt][qt]);
             }
@@ -283,16 +288,16 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
     // Every wave passes one barrier per key block on either path below.  The fast loop touches
     // O only through the matrix cores; a block whose maximum grows (always the first, rarely a
     // later one) leaves it and is finished by the rescaling path.
-    load_block(0);
-    store_block(0);
+    load_block(0, 0);
+    staged();
     __syncthreads();
     int kb = 0;
     for (;;) {
         for (; kb < n_kb; ++kb) {
-            if (kb + 1 < n_kb) load_block(kb + 1);
+            if (kb + 1 < n_kb) load_block(kb + 1, (kb + 1) & 1);
             if (active && scores(kb)) break;
             if (active) accumulate(kb);
-            if (kb + 1 < n_kb) store_block((kb + 1) & 1);
+            staged();
             __syncthreads();
         }
         if (kb >= n_kb) break;
@@ -306,7 +311,7 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
             for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
         }
         accumulate(kb);
-        if (kb + 1 < n_kb) store_block((kb + 1) & 1);
+        staged();
         __syncthreads();
         ++kb;
     }
