@@ -173,16 +173,24 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
     // P / VCH); the lane reads the chunk that its position holds.  Keys past L_kv read as zero.
     const int L_pad = ((a.L_kv + kFaKeys - 1) / kFaKeys) * kFaKeys;
     const __amdgpu_buffer_rsrc_t rsV = uniform_rsrc(a.Vt + ((size_t)u * a.H + h) * HD * L_pad, HD * L_pad * 2);
-    auto load_block = [&](int kb, int buf) {
-        char *Kl = lds + buf * L::BUF;
-        char *Vl = Kl + L::KBYTES;
+    // K(kb) and V^T(kb) go to the K and V^T halves of buffer kb & 1, on staggered schedules
+    // (K two blocks ahead, V^T one; see the loop below).
+    auto load_k = [&](int kb) {
+        char *Kl = lds + (kb & 1) * L::BUF;
 #pragma unroll
         for (int i = 0; i < L::CHUNKS; ++i) {
             const int P0 = (wv * L::CHUNKS + i) * 64, P = P0 + lane;
             const int kr = P / L::KCH, kc = (P % L::KCH) ^ (kr & (L::KCH - 1));
-            const int vr = P / L::VCH, vc = (P % L::VCH) ^ (vr & (L::VCH - 1));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (__attribute__((address_space(3))) void *)(Kl + 16 * P0), 16,
                                                      ((kb * kFaKeys + kr) * HD + 8 * kc) * 2, 0, 0, 0);
+        }
+    };
+    auto load_v = [&](int kb) {
+        char *Vl = lds + (kb & 1) * L::BUF + L::KBYTES;
+#pragma unroll
+        for (int i = 0; i < L::CHUNKS; ++i) {
+            const int P0 = (wv * L::CHUNKS + i) * 64, P = P0 + lane;
+            const int vr = P / L::VCH, vc = (P % L::VCH) ^ (vr & (L::VCH - 1));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (__attribute__((address_space(3))) void *)(Vl + 16 * P0), 16,
                                                      (vr * L_pad + kb * kFaKeys + 8 * vc) * 2, 0, 0, 0);
         }
@@ -203,18 +211,15 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
     }
 
     const int n_kb = (a.L_kv + kFaKeys - 1) / kFaKeys;
-    f32x4_t st[4][QT];
     float mb[QT];
-    // S^T tiles for block kb: keys 16*kt + 4g + i (rows) against queries 16*qt + j (columns);
-    // keys past L_kv (only in a partial last block) score -inf.  Then the block maxima
-    // (base-2 scaled); returns whether some row's maximum exceeds the reference by more
-    // than kFaSlack (the same answer on every lane of the wave).
-    auto scores = [&](int kb) -> bool {
+    // S^T tiles for block kb into S: keys 16*kt + 4g + i (rows) against queries 16*qt + j
+    // (columns), matrix cores only.
+    auto scores = [&](int kb, f32x4_t (&S)[4][QT]) {
         const char *Kl = lds + (kb & 1) * L::BUF;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt) st[kt][qt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            for (int qt = 0; qt < QT; ++qt) S[kt][qt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < TK; ++t) {
             u32x4_t qf[QT];
@@ -225,9 +230,14 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
             for (int kt = 0; kt < 4; ++kt) {
                 const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(Kl + L::kpos(16 * kt + j, 4 * t + g));
 #pragma unroll
-                for (int qt = 0; qt < QT; ++qt) st[kt][qt] = mfma_bf16(kf, qf[qt], st[kt][qt]);
+                for (int qt = 0; qt < QT; ++qt) S[kt][qt] = mfma_bf16(kf, qf[qt], S[kt][qt]);
             }
         }
+    };
+    // Keys past L_kv (only in a partial last block) score -inf; then the block maxima (base-2
+    // scaled) into mb.  Returns whether some row's maximum exceeds the reference by more than
+    // kFaSlack (the same answer on every lane of the wave).
+    auto block_max = [&](int kb, f32x4_t (&S)[4][QT]) -> bool {
         if (kb == n_kb - 1 && (a.L_kv % kFaKeys) != 0) {
             const int key0 = kb * kFaKeys + 4 * g;
 #pragma unroll
@@ -236,7 +246,7 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
                 for (int i = 0; i < 4; ++i)
                     if (key0 + 16 * kt + i >= a.L_kv)
 #pragma unroll
-                        for (int qt = 0; qt < QT; ++qt) st[kt][qt][i] = -__builtin_inff();
+                        for (int qt = 0; qt < QT; ++qt) S[kt][qt][i] = -__builtin_inff();
         }
         bool grow = false;
 #pragma unroll
@@ -245,15 +255,27 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[kt][qt][i]);
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[kt][qt][i]);
             mb[qt] = wave_max4(mx) * a.scale_log2;
             grow = grow || mb[qt] > m[qt] + kFaSlack;
         }
         return __builtin_amdgcn_readfirstlane(__ballot(grow) != 0 ? 1 : 0) != 0;
     };
-    // Weights against the reference maximum (below 2^kFaSlack), row sums, and
+    // The reference maximum moves to the block maxima in mb; O and the row sums follow.
+    auto rescale = [&]() {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            const float mnew = fmaxf(m[qt], mb[qt]);
+            const float alpha = __builtin_amdgcn_exp2f(m[qt] - mnew);
+            m[qt] = mnew;
+            l[qt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+        }
+    };
+    // Weights of S against the reference maximum (below 2^kFaSlack), row sums, and
     // O^T += V^T P^T with d rows 16*dt + j and key slots (32s + 4g .. +3, 32s + 16 + 4g .. +3).
-    auto accumulate = [&](int kb) {
+    auto accumulate = [&](int kb, const f32x4_t (&S)[4][QT]) {
         const char *Vl = lds + (kb & 1) * L::BUF + L::KBYTES;
         u32x4_t pf[2][QT];
 #pragma unroll
@@ -265,7 +287,7 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[kt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][qt][i], a.scale_log2, nm));
+                    p[kt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][qt][i], a.scale_log2, nm));
                     ls += p[kt][i];
                 }
             l[qt] += ls;
@@ -285,36 +307,40 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
             }
     };
 
-    // Every wave passes one barrier per key block on either path below.  The fast loop touches
-    // O only through the matrix cores; a block whose maximum grows (always the first, rarely a
-    // later one) leaves it and is finished by the rescaling path.
-    load_block(0, 0);
+    // Software-pipelined over key blocks: while block kb's weights and P V product run, the
+    // matrix cores also form block kb+1's scores, so the two can overlap.  At the top of
+    // iteration kb, K(kb+1) and V^T(kb) are in LDS; the iteration loads V^T(kb+1) (into the
+    // half that V^T(kb-1) used) and K(kb+2) (into the half of K(kb), whose scores were formed
+    // in the previous iteration), and every wave passes one barrier.  A block whose maximum
+    // grows (always the first, rarely a later one) moves the reference maximum after the
+    // previous block has been accumulated against the old one.
+    f32x4_t sc[4][QT], sn[4][QT];
+    load_k(0);
+    load_v(0);
+    if (n_kb > 1) load_k(1);
     staged();
     __syncthreads();
-    int kb = 0;
-    for (;;) {
-        for (; kb < n_kb; ++kb) {
-            if (kb + 1 < n_kb) load_block(kb + 1, (kb + 1) & 1);
-            if (active && scores(kb)) break;
-            if (active) accumulate(kb);
-            staged();
-            __syncthreads();
-        }
-        if (kb >= n_kb) break;
+    if (active) {
+        scores(0, sc);
+        if (block_max(0, sc)) rescale();
+    }
+    __syncthreads();   // K(0) is read; iteration 0 refills its half with K(2)
+    for (int kb = 0; kb + 1 < n_kb; ++kb) {
+        load_v(kb + 1);
+        if (kb + 2 < n_kb) load_k(kb + 2);
+        if (active) {
+            scores(kb + 1, sn);
+            accumulate(kb, sc);
+            if (block_max(kb + 1, sn)) rescale();
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-            const float mnew = fmaxf(m[qt], mb[qt]);
-            const float alpha = __builtin_amdgcn_exp2f(m[qt] - mnew);
-            m[qt] = mnew;
-            l[qt] *= alpha;
+            for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+                for (int qt = 0; qt < QT; ++qt) sc[kt][qt] = sn[kt][qt];
         }
-        accumulate(kb);
         staged();
         __syncthreads();
-        ++kb;
     }
+    if (active) accumulate(n_kb - 1, sc);
     if (!active) return;
     // O[b, h, 16*qt + j, 16*dt + 4g .. +3] = O^T / row sum.
     uint16_t *ob = Odst + qbase;
