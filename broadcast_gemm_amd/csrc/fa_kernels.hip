@@ -214,6 +214,21 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
     float mb[QT];
     // S^T tiles for block kb into S: keys 16*kt + 4g + i (rows) against queries 16*qt + j
     // (columns), matrix cores only.
+    // The wave's query fragments stay in registers for the whole loop (B operand: query
+    // 16*qt + j, d = 32t + 8g .. +7), read once from the rows the wave staged.
+    u32x4_t qf[TK][QT];
+#pragma unroll
+    for (int t = 0; t < TK; ++t)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+            qf[t][qt] = *reinterpret_cast<const u32x4_t *>(Ql + (16 * qt + j) * L::QROW + (32 * t + 8 * g) * 2);
+    // The lane's byte offsets of its K fragments (row 16*kt + j, chunk 4t + g: kpos, less the
+    // 16*kt rows, which do not change the swizzle) and V^T fragments (row 16*dt + j, chunk 4s + g).
+    int koff[TK], voff[2];
+#pragma unroll
+    for (int t = 0; t < TK; ++t) koff[t] = L::kpos(j, 4 * t + g);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) voff[s2] = L::vpos(j, 4 * s2 + g);
     auto scores = [&](int kb, f32x4_t (&S)[4][QT]) {
         const char *Kl = lds + (kb & 1) * L::BUF;
 #pragma unroll
@@ -222,15 +237,11 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
             for (int qt = 0; qt < QT; ++qt) S[kt][qt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < TK; ++t) {
-            u32x4_t qf[QT];
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt)
-                qf[qt] = *reinterpret_cast<const u32x4_t *>(Ql + (16 * qt + j) * L::QROW + (32 * t + 8 * g) * 2);
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
-                const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(Kl + L::kpos(16 * kt + j, 4 * t + g));
+                const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(Kl + koff[t] + 16 * kt * L::KROW);
 #pragma unroll
-                for (int qt = 0; qt < QT; ++qt) S[kt][qt] = mfma_bf16(kf, qf[qt], S[kt][qt]);
+                for (int qt = 0; qt < QT; ++qt) S[kt][qt] = mfma_bf16(kf, qf[t][qt], S[kt][qt]);
             }
         }
     };
@@ -301,7 +312,7 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const u32x4_t vf = *reinterpret_cast<const u32x4_t *>(Vl + L::vpos(16 * dt + j, 4 * s + g));
+                const u32x4_t vf = *reinterpret_cast<const u32x4_t *>(Vl + voff[s] + 16 * dt * L::VROW);
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = mfma_bf16(vf, pf[s][qt], oacc[dt][qt]);
             }
