@@ -110,10 +110,6 @@ __device__ __forceinline__ float wave_max4(float x) {
     x = fmaxf(x, __shfl_xor(x, 16));
     return fmaxf(x, __shfl_xor(x, 32));
 }
-__device__ __forceinline__ float wave_sum4(float x) {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
-}
 
 // WPC waves per candidate, each with 16*QT of its queries; kFaGroup candidates per block.
 template <int QT, int WPC, int HD>
@@ -203,12 +199,17 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    float m[QT], l[QT];
+    // Row sums of the weights, by the matrix cores: an all-ones A operand against the same P^T
+    // fragments leaves every row of lsum[qt] equal to query j's running sum (of the bf16 weights
+    // that multiply V).
+    float m[QT];
+    f32x4_t lsum[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         m[qt] = -__builtin_inff();
-        l[qt] = 0.0f;
+        lsum[qt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     }
+    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0 pairs
 
     const int n_kb = (a.L_kv + kFaKeys - 1) / kFaKeys;
     float mb[QT];
@@ -279,12 +280,12 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
             const float mnew = fmaxf(m[qt], mb[qt]);
             const float alpha = __builtin_amdgcn_exp2f(m[qt] - mnew);
             m[qt] = mnew;
-            l[qt] *= alpha;
+            lsum[qt] *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
         }
     };
-    // Weights of S against the reference maximum (below 2^kFaSlack), row sums, and
+    // Weights of S against the reference maximum (below 2^kFaSlack), their row sums, and
     // O^T += V^T P^T with d rows 16*dt + j and key slots (32s + 4g .. +3, 32s + 16 + 4g .. +3).
     auto accumulate = [&](int kb, const f32x4_t (&S)[4][QT]) {
         const char *Vl = lds + (kb & 1) * L::BUF + L::KBYTES;
@@ -292,22 +293,21 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
             const float nm = -m[qt];
-            float ls = 0.0f;
             float p[4][4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[kt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][qt][i], a.scale_log2, nm));
-                    ls += p[kt][i];
-                }
-            l[qt] += ls;
+                for (int i = 0; i < 4; ++i) p[kt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][qt][i], a.scale_log2, nm));
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 pf[s][qt] = (u32x4_t){pack_bf16x2(p[2 * s][0], p[2 * s][1]), pack_bf16x2(p[2 * s][2], p[2 * s][3]),
                                       pack_bf16x2(p[2 * s + 1][0], p[2 * s + 1][1]),
                                       pack_bf16x2(p[2 * s + 1][2], p[2 * s + 1][3])};
         }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) lsum[qt] = mfma_bf16(ones, pf[s][qt], lsum[qt]);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -357,7 +357,7 @@ __global__ void __launch_bounds__(64 * kFaGroup * WPC, 1) fa_fwd_kernel(FaArgs a
     uint16_t *ob = Odst + qbase;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-        const float inv = 1.0f / wave_sum4(l[qt]);
+        const float inv = 1.0f / lsum[qt][0];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const f32x4_t o = oacc[dt][qt];
