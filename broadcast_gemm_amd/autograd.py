@@ -27,7 +27,10 @@ from .rewrite import bucket_b_c, bucket_b_u
 
 
 class _BackwardPlans:
-    """Plans with the backward's workspace, keyed by (K_u, K_c, M, D), each sized to a batch range."""
+    """Plans with the backward's workspace, keyed by (K_u, K_c, M, D), each sized to a batch range.
+
+    A plan that a larger batch outgrows is dropped, not destroyed: autograd graphs recorded
+    with it may still run their backward, and it is freed once none refers to it."""
 
     def __init__(self, make_plan=LcePlan):
         self._make = make_plan
@@ -40,7 +43,6 @@ class _BackwardPlans:
             mu, mc = bucket_b_u(B_u), bucket_b_c(B_c)
             if plan is not None:
                 mu, mc = max(mu, plan.max_B_u), max(mc, plan.max_B_c)
-                plan.close()
             plan = self._make(mu, mc, K_u, K_c, M, D, dtype="bf16", flags=FLAG_BACKWARD)
             self._plans[key] = plan
         return plan

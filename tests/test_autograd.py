@@ -27,8 +27,11 @@ def test_backward_plans_are_sized_by_range_and_carry_the_backward_flag():
     assert (p.max_B_u, p.max_B_c, p.flags) == (16, 1024, FLAG_BACKWARD)
     assert t.plan_for(9, 300, 301, 197, 96, 160) is p
     q = t.plan_for(40, 4096, 301, 197, 96, 160)
-    assert p.closed and (q.max_B_u, q.max_B_c) == (64, 4096)
+    # an outgrown plan stays usable: a graph recorded with it may still run its backward
+    assert not p.closed and (q.max_B_u, q.max_B_c) == (64, 4096)
     assert t.plan_for(4, 10, 64, 32, 48, 128) is not q and len(made) == 3
+    t.close()
+    assert q.closed
 
 
 def test_module_parameters_and_init_scale():
