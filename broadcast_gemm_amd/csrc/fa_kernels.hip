@@ -13,7 +13,8 @@
 //
 // A wave holds 16*QT query rows of its candidate (a candidate's 64 queries take two waves,
 // so that everything a wave keeps stays within its share of the register file).  With v_mfma_f32_16x16x32_bf16 it forms
-// the transposed scores S^T = K Q^T (A: key rows, B: query rows, both read from LDS),
+// the transposed scores S^T = K Q^T (A: key rows from LDS, B: query rows, which the wave stages
+// through LDS once and then keeps in registers),
 // so lane (g, j) ends up with the scores of query j against keys 4g .. 4g+3 of every
 // 16-key tile.  Those are exactly the values it must supply for O^T = V^T P^T (B operand
 // P^T: query j, 8 keys), once the k slots of each 32-key step are taken as keys
