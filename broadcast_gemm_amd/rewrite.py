@@ -273,8 +273,6 @@ def _sdpa_args(node):
     if not _is_call(node, (F.scaled_dot_product_attention,)):
         return None
     names = ["query", "key", "value", "attn_mask", "dropout_p", "is_causal", "scale"]
-    if len(node.args) > len(names):                    # enable_gqa given by position: leave alone
-        return None
     got = dict(zip(names, node.args))
     got.update(node.kwargs)
     if got.get("attn_mask") is not None or got.get("dropout_p", 0.0) not in (0, 0.0) or got.get("is_causal", False):

@@ -27,8 +27,6 @@ class TargetAttention(torch.nn.Module):
             return F.scaled_dot_product_attention(Q, Kb, Vb, attn_mask=torch.ones(1, dtype=torch.bool))
         if self.variant == "k_only":
             return F.scaled_dot_product_attention(Q, Kb, V[torch.zeros_like(mp)])
-        if self.variant == "gqa_positional":
-            return F.scaled_dot_product_attention(Q, Kb, Vb, None, 0.0, False, None, True)
         if self.scale is None:
             return F.scaled_dot_product_attention(Q, Kb, Vb)
         return F.scaled_dot_product_attention(Q, Kb, Vb, scale=self.scale)
@@ -78,12 +76,11 @@ def test_rewritten_graph_keeps_the_math_on_cpu():
     assert torch.allclose(gm(Q, K, V, mp), ref, rtol=2e-2, atol=2e-2)
 
 
-@pytest.mark.parametrize("case", ["causal", "mask", "k_only", "gqa_positional", "float32", "head_dim_32", "L_q_48",
-                                  "scale_0"])
+@pytest.mark.parametrize("case", ["causal", "mask", "k_only", "float32", "head_dim_32", "L_q_48", "scale_0"])
 def test_rewrite_leaves_other_attention_alone(case):
     kw = {"float32": dict(dtype=torch.float32), "head_dim_32": dict(hd=32), "L_q_48": dict(L_q=48)}.get(case, {})
     Q, K, V, mp = small(**kw)
-    variant = case if case in ("causal", "mask", "k_only", "gqa_positional") else "plain"
+    variant = case if case in ("causal", "mask", "k_only") else "plain"
     gm = fx.symbolic_trace(TargetAttention(variant=variant, scale=0.0 if case == "scale_0" else None))
     try:
         n = rw.rewrite_attention(gm, Q, K, V, mp)
