@@ -66,7 +66,23 @@ struct ikbo_lce_plan_s {
     void *W_u_pad, *W_c_pad, *W_cat_pad, *X;
     float *P_u, *P_c, *P_b, *P_part;
     uint32_t *err, *ctr, *flagw, *state;
+    // Backward plans: the streams that dC and dU run on beside the caller's stream, and the
+    // events that order them (fork after the grouping launch, fork after the segment sums,
+    // join of each side stream).
+    hipStream_t side[2];
+    hipEvent_t ev[4];
 };
+
+namespace {
+
+void release_side(ikbo_lce_plan_s *p) {
+    for (hipEvent_t &e : p->ev)
+        if (e != nullptr) { (void)hipEventDestroy(e); e = nullptr; }
+    for (hipStream_t &st : p->side)
+        if (st != nullptr) { (void)hipStreamDestroy(st); st = nullptr; }
+}
+
+}  // namespace
 
 namespace {
 
@@ -349,6 +365,19 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
         if (p->fused_bpc < 1) { (void)hipFree(p->arena); delete p; return IKBO_ERR_UNSUPPORTED; }
         p->fused_grid = p->n_cu * p->fused_bpc;
     }
+    if (p->bwd) {
+        hipError_t se = hipSuccess;
+        for (hipStream_t &st : p->side)
+            if (se == hipSuccess) se = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+        for (hipEvent_t &ev : p->ev)
+            if (se == hipSuccess) se = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (se != hipSuccess) {
+            release_side(p);
+            (void)hipFree(p->arena);
+            delete p;
+            return hip_fail(se, "backward streams");
+        }
+    }
     *out = p;
     return IKBO_OK;
 }
@@ -365,6 +394,7 @@ int ikbo_lce_plan_destroy(ikbo_lce_plan_t p) {
     (void)hipGetDevice(&cur);
     if (cur != p->device) (void)hipSetDevice(p->device);
     hipError_t e = hipDeviceSynchronize();
+    release_side(p);
     hipError_t f = hipFree(p->arena);
     if (cur != p->device && cur >= 0) (void)hipSetDevice(cur);
     delete p;
@@ -658,6 +688,34 @@ int ikbo_lce_backward(ikbo_lce_plan_t p, const void *dY, const void *U, const vo
     pa.B_u = B_u; pa.B_c = B_c; pa.M = M; pa.K_u = K_u; pa.K_c = K_c; pa.ldw_dup = p->du_ldw;
     if ((e = launch_bwd_prep(pa, s)) != hipSuccess) return hip_fail(e, "bwd prep");
 
+    // After the grouping launch three chains are independent: dC, the segment sums and dU, and
+    // the weight gradients (which need the segment sums).  dC runs on side stream 0 and dU on
+    // side stream 1 beside the caller's stream, which waits for both before the call returns,
+    // so that work enqueued after it sees every output.  None of the chains waits on another
+    // inside a kernel, so running them side by side cannot stall.
+    const bool fork = env_int("IKBO_BWD_STREAMS", 1) != 0;
+    hipStream_t s_dc = s, s_du = s;
+    int joined = 0;
+    auto join = [&]() -> hipError_t {
+        hipError_t r = hipSuccess;
+        for (int i = 0; i < joined; ++i) {
+            if (r == hipSuccess) r = hipEventRecord(p->ev[2 + i], p->side[i]);
+            if (r == hipSuccess) r = hipStreamWaitEvent(s, p->ev[2 + i], 0);
+        }
+        joined = 0;
+        return r;
+    };
+    auto fail = [&](hipError_t err, const char *what) {
+        (void)join();
+        return hip_fail(err, what);
+    };
+    if (fork) {
+        if ((e = hipEventRecord(p->ev[0], s)) != hipSuccess) return hip_fail(e, "bwd fork");
+        if ((e = hipStreamWaitEvent(p->side[0], p->ev[0], 0)) != hipSuccess) return hip_fail(e, "bwd fork");
+        s_dc = p->side[0];
+        joined = 1;
+    }
+
     // dC[b] = W_c^T . dY[b] on the row-tile engine (W_c^T staged in LDS).
     if (B_c > 0) {
         RowArgs c{};
@@ -673,8 +731,11 @@ int ikbo_lce_backward(ikbo_lce_plan_t p, const void *dY, const void *U, const vo
         c.xcd_order = env_int("IKBO_BWD_DC_XCD", 1) != 0;   // a candidate's dc_nmc units share one L2
         c.spin_limit = p->spin_limit;
         const int grid = std::max(1, std::min(p->n_cu * p->dc_bpc, ceil_div(c.n_cand, kRowsBlock / 64)));
-        if (rows_lds_bytes(c) > (size_t)p->max_lds) return IKBO_ERR_UNSUPPORTED;
-        if ((e = launch_rows(EPI_STORE_T, p->dc_mb, c, grid, s)) != hipSuccess) return hip_fail(e, "bwd dC");
+        if (rows_lds_bytes(c) > (size_t)p->max_lds) {
+            (void)join();
+            return IKBO_ERR_UNSUPPORTED;
+        }
+        if ((e = launch_rows(EPI_STORE_T, p->dc_mb, c, grid, s_dc)) != hipSuccess) return fail(e, "bwd dC");
     }
 
     // S[u] = sum of dY over the user's candidates, as [bf16(S); bf16(S - hi)].
@@ -684,7 +745,13 @@ int ikbo_lce_backward(ikbo_lce_plan_t p, const void *dY, const void *U, const vo
     sa.B_u = B_u; sa.MD = MD;
     sa.L = std::max(4, ceil_div(B_c, p->seg_T));     // ceil(B_c / L) <= seg_T chunks
     sa.n_chunks = ceil_div(B_c, sa.L); sa.n_slices = p->seg_slices;
-    if ((e = launch_segsum(sa, s)) != hipSuccess) return hip_fail(e, "bwd segsum");
+    if ((e = launch_segsum(sa, s)) != hipSuccess) return fail(e, "bwd segsum");
+    if (fork) {
+        if ((e = hipEventRecord(p->ev[1], s)) != hipSuccess) return fail(e, "bwd fork");
+        if ((e = hipStreamWaitEvent(p->side[1], p->ev[1], 0)) != hipSuccess) return fail(e, "bwd fork");
+        s_du = p->side[1];
+        joined = 2;
+    }
 
     // dU[u] = [W_u^T | W_u^T] . [S_hi; S_lo] on the flat engine.
     TileGemmArgs ua{};
@@ -693,7 +760,7 @@ int ikbo_lce_backward(ikbo_lce_plan_t p, const void *dY, const void *U, const vo
     ua.BD = (long long)B_u * D;
     ua.n_ks = ceil_div(2 * M, 32); ua.n_ks_full = 2 * M / 32;
     ua.n_mchunks = p->du_nmc;
-    if ((e = launch_tile_gemm(DT_BF16, EPI_STORE_T, p->du_tile, ua, s)) != hipSuccess) return hip_fail(e, "bwd dU");
+    if ((e = launch_tile_gemm(DT_BF16, EPI_STORE_T, p->du_tile, ua, s_du)) != hipSuccess) return fail(e, "bwd dU");
 
     // Weight-gradient partials in one launch: sum over candidates of dY[b] . C[b]^T, and
     // over users of [S_hi; S_lo] . U[u]^T.
@@ -706,12 +773,13 @@ int ikbo_lce_backward(ikbo_lce_plan_t p, const void *dY, const void *U, const vo
     wu.E = B_u; wu.R = 2 * M; wu.N = K_u;
     wgrad_problem_setup(wu, p->wgu_chunks);
     wa.n_prob = 2; wa.D = D;
-    if ((e = launch_wgrad(wa, s)) != hipSuccess) return hip_fail(e, "bwd dW");
+    if ((e = launch_wgrad(wa, s)) != hipSuccess) return fail(e, "bwd dW");
 
     WgradReduceArgs ra{};
     ra.part_c = p->part_c; ra.part_u = p->part_u; ra.dW_c = dW_c; ra.dW_u = dW_u;
     ra.P_c = wc.n_chunks; ra.P_u = wu.n_chunks; ra.M = M; ra.K_u = K_u; ra.K_c = K_c;
-    if ((e = launch_wgrad_reduce(ra, s)) != hipSuccess) return hip_fail(e, "bwd reduce");
+    if ((e = launch_wgrad_reduce(ra, s)) != hipSuccess) return fail(e, "bwd reduce");
+    if ((e = join()) != hipSuccess) return hip_fail(e, "bwd join");
     return IKBO_OK;
 }
 

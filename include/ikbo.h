@@ -137,7 +137,10 @@ int ikbo_lce_forward(ikbo_lce_plan_t plan, const void *U, const void *C, const i
  * Every pointer except map must be 16-byte aligned (map: 4-byte).  Asynchronous, like
  * the forward: map entries outside [0, B_u) are skipped and reported by ikbo_lce_check
  * as IKBO_ERR_MAP_RANGE.  Uses the plan's workspace: do not overlap it with a forward
- * or another backward on the same plan in a different stream.
+ * or another backward on the same plan in a different stream.  dC and dU run on two
+ * streams that the plan owns, forked from `stream` by events after the work they need
+ * and joined back into it before the call returns: work enqueued on `stream` afterwards
+ * sees every output (under stream capture the fork and join are captured with it).
  * Errors (before anything is enqueued): INVALID_ARG, ALIGNMENT, UNSUPPORTED, HIP.
  */
 int ikbo_lce_backward(ikbo_lce_plan_t plan, const void *dY, const void *U, const void *C,
