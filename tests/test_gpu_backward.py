@@ -123,6 +123,40 @@ def test_backward_repeats_bit_exactly_and_plan_reuse():
         assert np.array_equal(p, r), f"{name}: larger plan differs"
 
 
+def test_backward_outputs_ordered_on_the_callers_stream():
+    """The call's kernels run on streams of the plan as well as the caller's; whatever the
+    caller enqueues on its stream after the call must see the finished outputs.  Three calls
+    on a user stream write the same output tensors, each with a different dY, and each is
+    copied on that stream right after its call, with no synchronisation in between; every
+    copy must equal the same call made alone."""
+    t = torch()
+    cfg = CONFIG_BY_NAME["default-70to1"].with_batch(8, 300)
+    log("[backward] outputs ordered on the caller's stream")
+    x = make_inputs(cfg)
+    dYs = [make_upstream_grad(cfg, seed=s) for s in (501, 502, 503)]
+    plan = bga.LcePlan(cfg.B_u, cfg.B_c, cfg.K_u, cfg.K_c, cfg.M, cfg.D, dtype="bf16", flags=bga.FLAG_BACKWARD)
+    try:
+        ins = tuple(to_dev(a) for a in (x.U, x.C, x.map, x.W_u, x.W_c))
+        dev_dY = [to_dev(d) for d in dYs]
+        alone = [tuple(to_f64(g) for g in plan.backward(d, *ins)) for d in dev_dY]
+        st = t.cuda.Stream()
+        st.wait_stream(t.cuda.current_stream())
+        with t.cuda.stream(st):
+            out = plan.backward(dev_dY[0], *ins)
+            copies = [tuple(g.clone() for g in out)]
+            for d in dev_dY[1:]:
+                plan.backward(d, *ins, out=out)
+                copies.append(tuple(g.clone() for g in out))
+        st.synchronize()
+        assert plan.check() == bga.IKBO_OK
+    finally:
+        plan.close()
+    for i, (c, a) in enumerate(zip(copies, alone)):
+        for name, g, r in zip(("dU", "dC", "dW_u", "dW_c"), c, a):
+            assert np.array_equal(to_f64(g), r), f"call {i}: {name} copied before the call finished"
+    assert not np.array_equal(alone[0][1], alone[1][1])
+
+
 def test_backward_edge_cases():
     """B_c = 0 zeroes dU and dW (outputs are overwritten, not accumulated); a map entry out
     of range is reported; a plan made without the backward flag is refused."""
