@@ -647,7 +647,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the IKBO LCE forward needs no collective, and "
-              f"--gpus {args.gpus} is not supported by this build.", file=sys.stderr)
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
         return 2
 
     import numpy as np
