@@ -225,17 +225,29 @@ def fa_weight_bound(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mp: np.ndarray,
 
 def tolerance_violations(Y_gpu: np.ndarray, Y_ref: np.ndarray, atol: float = 1e-3,
                          rtol: float = 1.6e-2, extra=None):
-    """Count elements with |Y_gpu - Y_ref| > atol + rtol*|Y_ref| (+ extra, elementwise, when
-    given) (bf16 inputs, fp32 accumulation: the acceptance bound of the IKBO LCE parity contract).  NaNs
-    count as violations unless both sides are NaN.  Returns (count, max_excess)."""
+    """Count elements outside the parity bar and return (count, max_excess).
+
+    A finite reference value r admits y when |y - r| <= atol + rtol*|r| (+ extra, elementwise,
+    when given): bf16 inputs and fp32 accumulation, the acceptance bound of the IKBO LCE parity
+    contract.  Special values must match exactly: an infinite reference admits only the same
+    infinity, a NaN reference only a NaN, and a NaN or infinite y only the same reference value.
+    A non-finite bound (an infinite or NaN ``extra``) admits nothing but exact equality.  The
+    excess of a special-value mismatch is reported as infinity."""
     Y_gpu = np.asarray(Y_gpu, dtype=np.float64)
-    err = np.abs(Y_gpu - Y_ref)
-    bound = atol + rtol * np.abs(Y_ref)
-    if extra is not None:
-        bound = bound + extra
-    both_nan = np.isnan(Y_gpu) & np.isnan(Y_ref)
-    same_inf = np.isinf(Y_gpu) & (Y_gpu == Y_ref)
-    bad = ~(err <= bound) & ~both_nan & ~same_inf
-    excess = np.where(bad, err - bound, 0.0)
-    ex = float(np.nanmax(excess)) if excess.size else 0.0
+    Y_ref = np.asarray(Y_ref, dtype=np.float64)
+    if Y_gpu.shape != Y_ref.shape:
+        raise ValueError(f"shape mismatch: {Y_gpu.shape} against {Y_ref.shape}")
+    fin = np.isfinite(Y_gpu) & np.isfinite(Y_ref)
+    with np.errstate(invalid="ignore", over="ignore"):
+        err = np.abs(Y_gpu - Y_ref)
+        bound = atol + rtol * np.abs(Y_ref)
+        if extra is not None:
+            bound = bound + np.asarray(extra, dtype=np.float64)
+    fin_ok = fin & np.isfinite(bound) & (err <= bound)
+    special_ok = ~fin & ((np.isnan(Y_gpu) & np.isnan(Y_ref)) | (Y_gpu == Y_ref))
+    exact_ok = fin & ~np.isfinite(bound) & (Y_gpu == Y_ref)
+    bad = ~(fin_ok | special_ok | exact_ok)
+    with np.errstate(invalid="ignore"):
+        excess = np.where(bad, np.where(fin & np.isfinite(bound), err - bound, np.inf), 0.0)
+    ex = float(excess.max()) if excess.size else 0.0
     return int(bad.sum()), ex
