@@ -31,7 +31,8 @@ if ROOT not in sys.path:
 METRIC = "IKBO-LCE fwd µs + TFLOP/s & HBM GB/s at B_c=1024, 70:1; % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-KERNEL_SOURCES = ["broadcast_gemm_amd/csrc/lce_rows.hip", "broadcast_gemm_amd/csrc/lce_rowtile.h",
+KERNEL_SOURCES = ["broadcast_gemm_amd/csrc/lce_stream.hip", "broadcast_gemm_amd/csrc/lce_stream.h",
+                  "broadcast_gemm_amd/csrc/lce_rows.hip", "broadcast_gemm_amd/csrc/lce_rowtile.h",
                   "broadcast_gemm_amd/csrc/lce_fused.hip", "broadcast_gemm_amd/csrc/lce_tile.h",
                   "broadcast_gemm_amd/csrc/lce_device.h", "broadcast_gemm_amd/csrc/lce_kernels.hip",
                   "broadcast_gemm_amd/csrc/lce_internal.h", "broadcast_gemm_amd/csrc/ikbo_api.cpp"]
@@ -40,6 +41,9 @@ KERNEL_SOURCES = ["broadcast_gemm_amd/csrc/lce_rows.hip", "broadcast_gemm_amd/cs
 def dominant_kernel(info: dict):
     """(name, launches per forward) of the forward's dominant kernel for a plan."""
     v, eng = info["variant"], info.get("engine")
+    if eng == "stream":
+        return {"S3": ("lce_stream_kernel (candidate)", 2),
+                "S4": ("lce_stream_kernel (user tiles + candidates, one launch)", 1)}.get(v, ("whole forward", 0))
     if eng == "rows":
         return {"S0": ("lce_rows_kernel (materialised X)", 3), "S2": ("lce_rows_kernel (candidate)", 4),
                 "S3": ("lce_rows_kernel (candidate)", 2),

@@ -1,13 +1,17 @@
 // ikbo_api.cpp -- the C ABI declared in include/ikbo.h: plans, validation,
 // workspace, and the launch sequence of each ladder stage.
 //
-// Two engines compute the products:
-//   rows  -- one wave per (batch entry, M chunk), all D columns of the entry,
-//            projection staged in LDS (lce_rows.hip); bf16 with D in
-//            {32, 64, 128, 160, 192} when the staged projection fits in LDS;
-//   flat  -- one wave per (128 flat columns, M chunk) over the B*D output
-//            columns (lce_kernels.hip, lce_fused.hip); every other case, and the
-//            narrow-load ladder stage S1.
+// Three engines compute the products:
+//   stream -- one wave per (batch entry, M chunk of up to all M rows), all D columns, every
+//             activation load 16 bytes wide, the user product cut into 16x16 tiles spread
+//             over every wave (lce_stream.hip); bf16 with D in {32, 64, 128, 160, 192}: the
+//             stages with the gather-add epilogue (S3, S4);
+//   rows   -- one wave per (batch entry, M chunk), all D columns of the entry,
+//             projection staged in LDS (lce_rows.hip); bf16 with D in
+//             {32, 64, 128, 160, 192} when the staged projection fits in LDS;
+//   flat   -- one wave per (128 flat columns, M chunk) over the B*D output
+//             columns (lce_kernels.hip, lce_fused.hip); every other case, and the
+//             narrow-load ladder stage S1.
 #include "ikbo.h"
 
 #include <hip/hip_runtime.h>
@@ -27,7 +31,7 @@ using namespace ikbo;
 
 namespace {
 
-enum Engine { ENGINE_FLAT = 0, ENGINE_ROWS = 1 };
+enum Engine { ENGINE_FLAT = 0, ENGINE_ROWS = 1, ENGINE_STREAM = 2 };
 
 }  // namespace
 
@@ -46,6 +50,10 @@ struct ikbo_lce_plan_s {
     int rows_mb;
     int rows_lds_shared;            // S4: W_u and W_c share one LDS region (their sum does not fit)
     int bpc_user, bpc_cand, bpc_both;
+    // stream engine
+    int st_mb, st_nmc, st_nrb, st_ncb;
+    int st_fused;                   // user tiles and candidates fit one launch's LDS
+    int st_tw;                      // tile-owning waves per workgroup in that launch
     // user split-K (fused paths and the rows engine's user launches)
     int ksplit, ks_per_split;
     uint32_t spin_limit;
@@ -113,6 +121,29 @@ int choose_mb(int n_mblocks, int max_mb) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int env_int(const char *name, int dflt);
+
+// Row blocks per streaming unit: the largest chunk (fewest wasted blocks among equals) whose
+// units for max_B_c candidates still give every wave of the grid one; when no chunk size does,
+// one row block per unit.  IKBO_STREAM_MB overrides the choice (tuning).
+int stream_choose_mb(int n_rb, int max_mb, int max_B_c, int n_waves) {
+    static const int sizes[] = {8, 6, 4, 3, 2, 1};
+    const int forced = env_int("IKBO_STREAM_MB", 0);
+    if (forced > 0) {
+        for (int mb : sizes)
+            if (mb <= forced && mb <= max_mb) return mb;
+    }
+    int best = 0, best_waste = 1 << 30;
+    for (int mb : sizes) {
+        if (mb > max_mb) continue;
+        const int n_mc = ceil_div(n_rb, mb);
+        if ((long long)max_B_c * n_mc < n_waves) continue;
+        const int waste = n_mc * mb - n_rb;
+        if (waste < best_waste) { best = mb; best_waste = waste; }
+    }
+    return best > 0 ? best : 1;
+}
 
 int env_int(const char *name, int dflt) {
     const char *v = getenv(name);
@@ -212,6 +243,52 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
         p->M_pad = p->n_mchunks * p->tile.mb * 16;
     }
 
+    // ---- the streaming engine takes the stages with the gather-add epilogue ----
+    // By default the two-launch stage; IKBO_STREAM=1 puts the one-launch stage on it too, 0
+    // keeps both on the row-tile engine.
+    const int stream_env = env_int("IKBO_STREAM", -1);
+    const bool stream_wanted = stream_env < 0 ? variant == IKBO_S3_EPILOGUE_FUSED
+                                              : (stream_env != 0 && (variant == IKBO_S3_EPILOGUE_FUSED ||
+                                                                     variant == IKBO_S4_PERSISTENT));
+    if (dtype == IKBO_DTYPE_BF16 && stream_wanted && stream_supported(D)) {
+        StreamArgs la{};
+        la.M = M; la.K_u = K_u; la.K_wc = K_c; la.n_ks_u = ceil_div(K_u, 32);
+        auto lds_of = [&](int units, int tiles, int tw) {
+            la.n_units = units; la.n_utiles = tiles; la.tile_waves = tw;
+            stream_lds_layout(la);
+            return stream_lds_bytes(la);
+        };
+        const size_t l_c = lds_of(1, 0, 4), l_u = lds_of(0, 1, 4);
+        const int mb = stream_choose_mb(n_mblocks, stream_max_mb(D), max_B_c, p->n_cu * (kStreamBlock / 64));
+        const int nmc = ceil_div(n_mblocks, mb);
+        const int bc = l_c <= (size_t)max_lds ? stream_blocks_per_cu(EPI_ADD_USER, D, mb, l_c) : 0;
+        const int bu = l_u <= (size_t)max_lds ? stream_blocks_per_cu(EPI_ADD_USER, D, mb, l_u) : 0;
+        // One launch: as many tile-owning waves per workgroup as the LDS holds next to W_c.
+        int bf = 0, tw = 4;
+        for (; tw >= 1 && bf < 1; tw /= 2) {
+            const size_t l_f = lds_of(1, 1, tw);
+            bf = l_f <= (size_t)max_lds ? stream_blocks_per_cu(EPI_ADD_USER, D, mb, l_f) : 0;
+            if (bf >= 1) break;
+        }
+        // Byte offsets within one fp32 [M][D] matrix and one [K][D] matrix are 32-bit.
+        if (bc >= 1 && bu >= 1 && (long long)M * D * 4 < (1LL << 31) &&
+            (long long)std::max(K_u, K_c) * D * 2 < (1LL << 31)) {
+            p->engine = ENGINE_STREAM;
+            p->st_mb = mb;
+            p->st_nmc = nmc;
+            p->st_nrb = n_mblocks;
+            p->st_ncb = D / 16;
+            p->st_fused = bf >= 1 ? 1 : 0;
+            p->st_tw = bf >= 1 ? tw : 4;
+            p->bpc_cand = bc;
+            p->bpc_user = bu;
+            p->bpc_both = bf;
+            p->n_mchunks = nmc;
+            p->M_pad = nmc * mb * 16;
+            p->rows_mb = mb;
+        }
+    }
+
     // ---- user K split (flat engine's fused kernel; the rows engine streams all of K) ----
     const int n_ks_u = ceil_div(K_u, 32), n_ks_c = ceil_div(K_c, 32);
     int kps;
@@ -271,7 +348,9 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     const size_t pc_bytes = (size_t)max_B_c * M * D * 4;
     const size_t n_units = (size_t)std::max(p->n_ucols_max, max_B_u) * p->n_mchunks;
     const size_t o_ctr = take(n_units * 4);
-    const size_t o_flag = take((std::max(n_units, (size_t)max_B_u * n_mblocks) + 2 + 2 * (size_t)p->n_mchunks) * 4);
+    const size_t n_tiles = (size_t)max_B_u * n_mblocks * (D / 16 > 0 ? D / 16 : 1);   // stream engine's user tiles
+    const size_t o_flag =
+        take((std::max(std::max(n_units, (size_t)max_B_u * n_mblocks), n_tiles) + 2 + 2 * (size_t)p->n_mchunks) * 4);
     size_t o_wu = 0, o_wc = 0, o_wcat = 0, o_x = 0, o_pu = 0, o_pc = 0, o_pb = 0, o_part = 0;
     const bool flat = p->engine == ENGINE_FLAT;
     if (variant == IKBO_S0_MATERIALISED) {
@@ -338,7 +417,7 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     e = hipMemcpy(p->state, &one, sizeof one, hipMemcpyHostToDevice);
     if (e != hipSuccess) { (void)hipFree(p->arena); delete p; return hip_fail(e, "hipMemcpy(state)"); }
 
-    // ---- persistent grid sizes ----
+    // ---- persistent grid sizes (the streaming engine's were taken with its choice) ----
     if (p->engine == ENGINE_ROWS) {
         RowArgs r{};
         r.M = M; r.M_pad = p->M_pad; r.K_u = K_u;
@@ -360,7 +439,7 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
             delete p;
             return IKBO_ERR_UNSUPPORTED;
         }
-    } else if (variant == IKBO_S4_PERSISTENT) {
+    } else if (p->engine == ENGINE_FLAT && variant == IKBO_S4_PERSISTENT) {
         p->fused_bpc = fused_blocks_per_cu(dtype, p->tile);
         if (p->fused_bpc < 1) { (void)hipFree(p->arena); delete p; return IKBO_ERR_UNSUPPORTED; }
         p->fused_grid = p->n_cu * p->fused_bpc;
@@ -406,7 +485,7 @@ int ikbo_lce_plan_destroy(ikbo_lce_plan_t p) {
 int ikbo_lce_plan_info(ikbo_lce_plan_t p, char *json, size_t cap) {
     if (p == nullptr || (json == nullptr && cap > 0)) return IKBO_ERR_INVALID_ARG;
     static const char *names[] = {"AUTO", "S0", "S1", "S2", "S3", "S4"};
-    const bool rows = p->engine == ENGINE_ROWS;
+    const bool rows = p->engine != ENGINE_FLAT;
     char buf[1536];
     int n = snprintf(buf, sizeof buf,
                      "{\"variant\":\"%s\",\"dtype\":\"%s\",\"engine\":\"%s\",\"max_B_u\":%d,\"max_B_c\":%d,"
@@ -415,7 +494,8 @@ int ikbo_lce_plan_info(ikbo_lce_plan_t p, char *json, size_t cap) {
                      "\"user_ksteps_per_split\":%d,\"blocks_per_cu\":[%d,%d,%d],\"fused_grid\":%d,"
                      "\"n_cu\":%d,\"workspace_bytes\":%zu,\"backward\":%d,\"bwd_dc_mb\":%d,"
                      "\"bwd_du_mb\":%d,\"bwd_seg_chunks\":%d,\"bwd_wgc_chunks\":%d,\"bwd_wgu_chunks\":%d}",
-                     names[p->variant], p->dtype == IKBO_DTYPE_BF16 ? "bf16" : "f32", rows ? "rows" : "flat",
+                     names[p->variant], p->dtype == IKBO_DTYPE_BF16 ? "bf16" : "f32",
+                     p->engine == ENGINE_STREAM ? "stream" : rows ? "rows" : "flat",
                      p->max_B_u, p->max_B_c, p->K_u, p->K_c, p->M, p->D, rows ? p->rows_mb : p->tile.mb,
                      p->n_mchunks, p->M_pad, rows ? 0 : p->tile.vec, p->ldw_u, p->ldw_c, p->ldw_cat, p->ksplit,
                      p->ks_per_split, p->bpc_user, p->bpc_cand, p->bpc_both, p->fused_grid, p->n_cu,
@@ -548,6 +628,58 @@ int forward_rows(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t 
     return IKBO_OK;
 }
 
+int forward_stream(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t *map, const void *W_u,
+                   const void *W_c, void *Y, int B_u, int B_c, hipStream_t s) {
+    StreamArgs a{};
+    a.U = static_cast<const uint16_t *>(U);
+    a.C = static_cast<const uint16_t *>(C);
+    a.W_u = static_cast<const uint16_t *>(W_u);
+    a.W_c = static_cast<const uint16_t *>(W_c);
+    a.map = map;
+    a.out = Y;
+    a.P_u = p->P_u;
+    a.flags = p->flagw;
+    a.err = p->err;
+    a.B_u = B_u; a.M = p->M; a.D = p->D;
+    a.K_u = p->K_u; a.K_c = p->K_c; a.K_wc = p->K_c;
+    a.n_ks_u = ceil_div(p->K_u, 32); a.n_ks_c = ceil_div(p->K_c, 32);
+    a.n_rb = p->st_nrb; a.n_cb = p->st_ncb; a.n_mc = p->st_nmc;
+    a.xcd_order = env_int("IKBO_STREAM_XCD", 1) != 0;
+    a.spin_limit = p->spin_limit;
+    a.debug_flags = p->flags;
+    const int n_tiles = B_u * p->st_nrb * p->st_ncb;
+    const int n_units = B_c * p->st_nmc;
+    auto launch = [&](StreamArgs x, int bpc) -> hipError_t {
+        stream_lds_layout(x);
+        if (stream_lds_bytes(x) > (size_t)p->max_lds) return hipErrorInvalidValue;
+        const int blocks = std::max(ceil_div(x.n_units, kStreamBlock / 64), ceil_div(x.n_utiles, x.tile_waves));
+        const int grid = std::max(1, std::min(p->n_cu * bpc, blocks));
+        return launch_stream(EPI_ADD_USER, p->st_mb, x, grid, s);
+    };
+    hipError_t e;
+    if (p->variant == IKBO_S4_PERSISTENT && p->st_fused) {
+        // One launch needs a fresh epoch per forward: a captured launch would replay a baked
+        // epoch and meet its own old flags, so capture takes the two-launch sequence.
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if ((e = hipStreamIsCapturing(s, &cap)) != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+        if (cap == hipStreamCaptureStatusNone) {
+            StreamArgs f = a;
+            f.n_utiles = n_tiles; f.n_units = n_units; f.wait_flags = 1; f.tile_waves = p->st_tw;
+            f.epoch = ++p->epoch;
+            if (f.epoch == 0) f.epoch = ++p->epoch;   // 0 is the flags' initial value
+            if ((e = launch(f, p->bpc_both)) != hipSuccess) return hip_fail(e, "fused");
+            return IKBO_OK;
+        }
+    }
+    StreamArgs u = a;
+    u.n_utiles = n_tiles; u.n_units = 0; u.tile_waves = 4;
+    if ((e = launch(u, p->bpc_user)) != hipSuccess) return hip_fail(e, "user tiles");
+    StreamArgs c = a;
+    c.n_utiles = 0; c.n_units = n_units; c.wait_flags = 0; c.tile_waves = 4;   // stream order publishes P_u
+    if ((e = launch(c, p->bpc_cand)) != hipSuccess) return hip_fail(e, "cand gemm");
+    return IKBO_OK;
+}
+
 int forward_flat(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t *map, const void *W_u,
                  const void *W_c, void *Y, int B_u, int B_c, hipStream_t s) {
     const int K_u = p->K_u, K_c = p->K_c, M = p->M, D = p->D, dt = p->dtype;
@@ -657,6 +789,7 @@ int ikbo_lce_forward(ikbo_lce_plan_t p, const void *U, const void *C, const int3
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     if (cur != p->device) return IKBO_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p->engine == ENGINE_STREAM) return forward_stream(p, U, C, map, W_u, W_c, Y, B_u, B_c, s);
     if (p->engine == ENGINE_ROWS) return forward_rows(p, U, C, map, W_u, W_c, Y, B_u, B_c, s);
     return forward_flat(p, U, C, map, W_u, W_c, Y, B_u, B_c, s);
 }

@@ -139,6 +139,45 @@ size_t rows_lds_bytes(const RowArgs &a);   // dynamic LDS of one launch (staged 
 int rows_blocks_per_cu(int epi, int D, int mb, size_t lds_bytes);
 hipError_t launch_rows(int epi, int mb, const RowArgs &a, int grid, hipStream_t s);
 
+// ---- streaming engine (lce_stream.hip; bf16, D in {32, 64, 128, 160, 192}) ---------------
+
+constexpr int kStreamBlock = 256;   // 4 waves: one per SIMD, up to 512 registers each
+
+// One launch: user tiles first (P_u[u] in 16x16 tiles, spread over every wave), then the
+// candidate units (b, M chunk of 16*MB rows), static round-robin over the waves.
+struct StreamArgs {
+    const uint16_t *U, *C;        // U [B_u][K_u][D]; C [B][K_c][D]
+    const uint16_t *W_u;          // [M][K_u]
+    const uint16_t *W_c;          // [M][K_wc]; K_wc >= K_c (columns past K_c are never used)
+    const int32_t *map;
+    void *out;                    // Y (bf16) or P_c (fp32) [B][M][D]
+    float *P_u;                   // [B_u][M][D]
+    uint32_t *flags;              // [B_u][n_rb][n_cb] tile flags (epochs)
+    uint32_t *err;
+    uint32_t epoch;
+    int B_u, M, D;
+    int K_u, K_c, K_wc;
+    int n_ks_u, n_ks_c;
+    int n_rb, n_cb;               // ceil(M / 16), D / 16: user tiles per user = n_rb * n_cb
+    int n_mc;                     // candidate units per batch entry (16*MB rows each)
+    int n_utiles;                 // user tiles in this launch (B_u * n_rb * n_cb or 0)
+    int n_units;                  // candidate units in this launch (B * n_mc or 0)
+    int wait_flags;               // candidates poll the user tiles' flags (users in the same launch)
+    int xcd_order;                // schedule numbers blocks XCD by XCD
+    int tile_waves;               // waves per workgroup that own user tiles (1, 2 or 4)
+    int lds_wc, lds_wu, lds_us;   // LDS byte offsets: W_c copy, W_u copy, user slices (per owner us_bytes)
+    int us_bytes;
+    uint32_t spin_limit;
+    uint32_t debug_flags;
+};
+
+bool stream_supported(int D);
+int stream_max_mb(int D);
+void stream_lds_layout(StreamArgs &a);    // fills lds_* / us_bytes from the launch's work
+size_t stream_lds_bytes(const StreamArgs &a);
+int stream_blocks_per_cu(int epi, int D, int mb, size_t lds_bytes);
+hipError_t launch_stream(int epi, int mb, const StreamArgs &a, int grid, hipStream_t s);
+
 // ---- backward (lce_backward.hip) -----------------------------------------------------------
 
 constexpr int kBwdPrepBlock = 1024;

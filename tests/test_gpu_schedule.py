@@ -44,19 +44,23 @@ def _cases():
             # S0's packed [W_u | W_c] (M x (K_u + K_c)) must fit LDS for the rows engine.
             if v == "S0" and sh[4] * (sh[2] + sh[3]) * 2 > 150 * 1024:
                 continue
-            yield pytest.param(sh, v, id=f"{sid}-{v}")
+            # the gather-add stages run on both engines (the streaming one and the row-tile one)
+            for eng in (["stream", "rows"] if v in ("S3", "S4") else ["rows"]):
+                yield pytest.param(sh, v, eng, id=f"{sid}-{v}-{eng}")
 
 
-@pytest.mark.parametrize("shape,variant", list(_cases()))
-def test_schedule_shapes(shape, variant):
+@pytest.mark.parametrize("shape,variant,engine", list(_cases()))
+def test_schedule_shapes(shape, variant, engine, monkeypatch):
     import oracle
     B_u, B_c, K_u, K_c, M, D, mp = shape
-    log(f"[schedule] shape={shape} variant={variant}")
+    log(f"[schedule] shape={shape} variant={variant} engine={engine}")
     cfg = LceConfig("schedule", B_u, B_c, K_u, K_c, M, D, "bf16", mp, 91)
     x = make_inputs(cfg)
+    if variant in ("S3", "S4"):
+        monkeypatch.setenv("IKBO_STREAM", "1" if engine == "stream" else "0")
     plan = bga.LcePlan(B_u, B_c, K_u, K_c, M, D, dtype="bf16", variant=variant)
     try:
-        assert plan.info()["engine"] == "rows"
+        assert plan.info()["engine"] == engine
         Y = plan.forward(*dev_inputs(x))
         st = plan.check()
         assert st == bga.IKBO_OK, bga.status_str(st)
