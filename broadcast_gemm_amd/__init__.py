@@ -44,7 +44,7 @@ FLAG_DEBUG_SKIP_USER = 4
 FLAG_BACKWARD = 8
 
 # Every symbol include/ikbo.h declares.
-EXPORTED = ("ikbo_lce_plan", "ikbo_lce_forward", "ikbo_lce_backward", "ikbo_lce_check",
+EXPORTED = ("ikbo_lce_plan", "ikbo_lce_forward", "ikbo_lce_forward_noalloc", "ikbo_lce_backward", "ikbo_lce_check",
             "ikbo_fa_plan", "ikbo_fa_forward", "ikbo_fa_forward_fused", "ikbo_fa_check", "ikbo_fa_plan_destroy", "ikbo_lce_plan_info",
             "ikbo_lce_plan_set_spin_limit", "ikbo_lce_plan_destroy", "ikbo_status_str",
             "ikbo_last_error_message")
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.ikbo_lce_plan.restype = ip
         L.ikbo_lce_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
         L.ikbo_lce_forward.restype = ip
+        L.ikbo_lce_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+        L.ikbo_lce_forward_noalloc.restype = ip
         L.ikbo_lce_backward.argtypes = [vp] + [vp] * 10 + [i] * 6 + [vp]
         L.ikbo_lce_backward.restype = ip
         L.ikbo_fa_plan.argtypes = [ctypes.POINTER(vp), i, i, i, i, i, i, i, ctypes.c_uint]
@@ -121,6 +123,34 @@ def _stream_handle(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def forward_noalloc_ptrs(U: int, C: int, mp: int, W_u: int, W_c: int, Y: int, B_u: int, B_c: int,
+                         K_u: int, K_c: int, M: int, D: int, stream: Optional[int] = None) -> int:
+    """Raw ``ikbo_lce_forward_noalloc`` call on device pointers; returns the status code."""
+    return lib().ikbo_lce_forward_noalloc(U, C, mp, W_u, W_c, Y, B_u, B_c, K_u, K_c, M, D, stream)
+
+
+def forward_noalloc(U, C, mp, W_u, W_c, out, stream=None):
+    """Y = W_u . U[map] + W_c . C into ``out`` without a plan and without allocating device
+    memory (``ikbo_lce_forward_noalloc``; bf16 tensors on the GPU).  Returns ``out``."""
+    torch = _torch()
+    for name, t in (("U", U), ("C", C), ("W_u", W_u), ("W_c", W_c), ("out", out)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor on the GPU")
+    if mp.dtype != torch.int32 or not mp.is_contiguous():
+        raise ValueError("map must be a contiguous int32 tensor")
+    B_u, K_u, D = U.shape
+    B_c, K_c = C.shape[0], C.shape[1]
+    M = W_u.shape[0]
+    if tuple(C.shape) != (B_c, K_c, D) or tuple(W_c.shape) != (M, K_c) or tuple(W_u.shape) != (M, K_u) \
+            or tuple(out.shape) != (B_c, M, D) or tuple(mp.shape) != (B_c,):
+        raise IkboError(IKBO_ERR_INVALID_ARG, "inconsistent shapes")
+    st = forward_noalloc_ptrs(U.data_ptr(), C.data_ptr(), mp.data_ptr(), W_u.data_ptr(), W_c.data_ptr(),
+                              out.data_ptr(), B_u, B_c, K_u, K_c, M, D, _stream_handle(stream))
+    if st != IKBO_OK:
+        raise IkboError(st, "ikbo_lce_forward_noalloc")
+    return out
 
 
 class LcePlan:

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libikbo.so")
-SOURCES = ["ikbo_api.cpp", "lce_kernels.hip", "lce_fused.hip", "lce_rows.hip", "lce_stream.hip", "lce_backward.hip", "ikbo_fa.cpp",
+SOURCES = ["ikbo_api.cpp", "lce_kernels.hip", "lce_fused.hip", "lce_rows.hip", "lce_stream.hip", "lce_noalloc.hip", "lce_backward.hip", "ikbo_fa.cpp",
            "fa_kernels.hip"]
 ARCH = os.environ.get("IKBO_OFFLOAD_ARCH", "gfx950")
 

@@ -10,6 +10,8 @@ namespace ikbo {
 
 // Record "what: <HIP error text>" for ikbo_last_error_message (ikbo_api.cpp); returns IKBO_ERR_HIP.
 int hip_fail(hipError_t e, const char *what);
+// Record `what` for ikbo_last_error_message; returns status.
+int status_fail(int status, const char *what);
 
 constexpr int kFaGroup = 4;       // candidates of one user per block (one wave each)
 constexpr int kFaKeys = 64;       // keys per staged K/V block

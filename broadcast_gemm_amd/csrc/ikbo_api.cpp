@@ -103,6 +103,11 @@ int ikbo::hip_fail(hipError_t e, const char *what) {
     return IKBO_ERR_HIP;
 }
 
+int ikbo::status_fail(int status, const char *what) {
+    g_last_error = what;
+    return status;
+}
+
 namespace {
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -124,10 +129,18 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int env_int(const char *name, int dflt);
 
+int env_int(const char *name, int dflt) {
+    const char *v = getenv(name);
+    if (v == nullptr || *v == '\0') return dflt;
+    return atoi(v);
+}
+
+}  // namespace
+
 // Row blocks per streaming unit: the largest chunk (fewest wasted blocks among equals) whose
 // units for max_B_c candidates still give every wave of the grid one; when no chunk size does,
 // one row block per unit.  IKBO_STREAM_MB overrides the choice (tuning).
-int stream_choose_mb(int n_rb, int max_mb, int max_B_c, int n_waves) {
+int ikbo::stream_choose_mb(int n_rb, int max_mb, int max_B_c, int n_waves) {
     static const int sizes[] = {8, 6, 4, 3, 2, 1};
     const int forced = env_int("IKBO_STREAM_MB", 0);
     if (forced > 0) {
@@ -145,13 +158,6 @@ int stream_choose_mb(int n_rb, int max_mb, int max_B_c, int n_waves) {
     return best > 0 ? best : 1;
 }
 
-int env_int(const char *name, int dflt) {
-    const char *v = getenv(name);
-    if (v == nullptr || *v == '\0') return dflt;
-    return atoi(v);
-}
-
-}  // namespace
 
 extern "C" {
 

@@ -172,6 +172,7 @@ struct StreamArgs {
 };
 
 bool stream_supported(int D);
+int stream_choose_mb(int n_rb, int max_mb, int max_B_c, int n_waves);   // row blocks per unit (ikbo_api.cpp)
 int stream_max_mb(int D);
 void stream_lds_layout(StreamArgs &a);    // fills lds_* / us_bytes from the launch's work
 size_t stream_lds_bytes(const StreamArgs &a);

@@ -113,6 +113,29 @@ int ikbo_lce_forward(ikbo_lce_plan_t plan, const void *U, const void *C, const i
                      int B_u, int B_c, int K_u, int K_c, int M, int D, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the forward above without
+ * a plan, calling no hipMalloc, hipFree or other allocating routine.  It computes
+ * the same Y as the two-launch gather-add stage (S3) on the streaming engine, and
+ * keeps the float32 user partial P_u [B_u, M, D] in a file-scope device array of
+ * IKBO_NOALLOC_SCRATCH_BYTES bytes (256 of them reserved) that every GPU the
+ * library runs on holds until the process ends.  Limits: bf16 only, D in
+ * {32, 64, 128, 160, 192}, and B_u*M*D*4 <= IKBO_NOALLOC_SCRATCH_BYTES - 256;
+ * beyond them it returns IKBO_ERR_UNSUPPORTED (ikbo_last_error_message says which)
+ * before anything is enqueued.  Arguments, layouts, alignment and the other errors
+ * are those of ikbo_lce_forward (the dimensions are not checked against a plan).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (two streams, two host threads) race and may produce wrong Y.  Map entries
+ * outside [0, B_u) leave their candidates' Y rows unwritten; this entry point does
+ * not report them.  The first call on a device also looks up the array's device
+ * address (no allocation).
+ */
+#define IKBO_NOALLOC_SCRATCH_BYTES (8u << 20)
+int ikbo_lce_forward_noalloc(const void *U, const void *C, const int32_t *map,
+                             const void *W_u, const void *W_c, void *Y,
+                             int B_u, int B_c, int K_u, int K_c, int M, int D, void *stream);
+
+/*
  * Enqueue the gradients of L = <dY, Y> for the forward above (the chain rule of the
  * pages' definition, blog "Deep Dive: Linear Compression", stage 1; the aibriefing
  * article's three-layers paragraph says the kernels serve training when the ratio

@@ -117,3 +117,16 @@ def test_fa_rejects_bad_arguments_before_hip(L):
     assert h.value is None
     assert L.ikbo_fa_forward(None, None, None, None, None, None, 1, 1, 4, 64, 100, 128, 0.0, None) == \
         bga.IKBO_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_bad_arguments_before_hip(L):
+    f = L.ikbo_lce_forward_noalloc
+    p = 1 << 20   # stand-in addresses: every check below returns before any HIP call
+    assert f(None, p, p, p, p, p, 2, 8, 32, 32, 16, 32, None) == bga.IKBO_ERR_INVALID_ARG
+    assert f(p, p, p, p, p, p, 0, 8, 32, 32, 16, 32, None) == bga.IKBO_ERR_INVALID_ARG
+    assert f(p, p, p, p, p, p, 2, 0, 32, 32, 16, 32, None) == bga.IKBO_OK            # no candidates: no-op
+    assert f(p + 8, p, p, p, p, p, 2, 8, 32, 32, 16, 32, None) == bga.IKBO_ERR_ALIGNMENT
+    assert f(p, p, p + 2, p, p, p, 2, 8, 32, 32, 16, 32, None) == bga.IKBO_ERR_ALIGNMENT
+    assert f(p, p, p, p, p, p, 2, 8, 32, 32, 16, 48, None) == bga.IKBO_ERR_UNSUPPORTED  # width
+    assert f(p, p, p, p, p, p, 200, 8, 32, 32, 96, 160, None) == bga.IKBO_ERR_UNSUPPORTED  # P_u > scratch
+    assert "scratch" in bga.last_error_message()
