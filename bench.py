@@ -684,11 +684,20 @@ def main() -> int:
         return run_backward(args, cfg, x)
     base = [dev(a) for a in (x.U, x.C, x.map, x.W_u, x.W_c)]
     tdt = base[0].dtype
-    set_bytes = sum(t.numel() * t.element_size() for t in base) + cfg.B_c * cfg.M * cfg.D * base[0].element_size()
+    set_bytes = sum(t.numel() * t.element_size() for t in base[:2]) + cfg.B_c * cfg.M * cfg.D * base[0].element_size()
     n_sets = max(1, math.ceil(args.rotate_mb * 2**20 / set_bytes))
     sets = []
     for i in range(n_sets):
-        ins = base if i == 0 else [t.clone() for t in base]
+        if i == 0:
+            ins = base
+        else:
+            # Each further set draws its own U and C (N(0,1), as the seeded generator does, from
+            # a distinct seed); the map and the projections are the workload's and stay shared.
+            g = torch.Generator(device="cuda")
+            g.manual_seed(cfg.seed + 7919 * i)
+            U_i = torch.randn(tuple(base[0].shape), generator=g, device="cuda", dtype=torch.float32).to(tdt)
+            C_i = torch.randn(tuple(base[1].shape), generator=g, device="cuda", dtype=torch.float32).to(tdt)
+            ins = [U_i, C_i] + base[2:]
         Y = torch.empty((cfg.B_c, cfg.M, cfg.D), dtype=tdt, device="cuda")
         sets.append(ins + [Y])
     if args.mode == "rewrite":

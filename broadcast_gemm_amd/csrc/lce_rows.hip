@@ -24,10 +24,9 @@
 // Publication without cache maintenance: a user unit writes P_u through to
 // memory (device-scope stores), waits for the acknowledgements and only then
 // stores the launch epoch in its flag.  A candidate that has read the flag
-// reads P_u with ordinary loads: no wave of the launch touched those lines
-// before they were final, and caches start the launch clean, so no cache can
-// hold an older copy.  Agent-scope fences would instead write back or
-// invalidate a whole L2 per use.
+// reads P_u with device-scope loads (sc1), which are served from the coherent
+// level and never from a stale line of its own XCD's L2 or its CU's cache.
+// Agent-scope fences would instead write back or invalidate a whole L2 per use.
 //
 // There is no device-wide work counter: contended atomics on one address
 // serialise at about 12 ns each, more than the whole schedule is worth.  The
@@ -92,24 +91,27 @@ struct Rows {
     }
     static constexpr int row_so(int mb, int r, int elt) { return (16 * mb + r) * D * elt; }
 
-    // The NT fp32 values this lane owns in each of the 4 rows of block mb.
+    // The NT fp32 values this lane owns in each of the 4 rows of block mb, read with cache
+    // policy AUX (kSc1 for P_u: device scope, as the lines were written through by other XCDs
+    // during the launch).
+    template <int AUX = kSc1>
     static __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rs, int o1, int o2, int mb,
                                                       float (&v)[4][NT]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int so = row_so(mb, r, 4);
             if constexpr (N8 != 0) {
-                const f32x4_t x0 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, o1, so, 0));
-                const f32x4_t x1 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, o1 + 16, so, 0));
+                const f32x4_t x0 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, o1, so, AUX));
+                const f32x4_t x1 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, o1 + 16, so, AUX));
 #pragma unroll
                 for (int t = 0; t < 4; ++t) { v[r][t] = x0[t]; v[r][4 + t] = x1[t]; }
             }
             if constexpr (W2 == 2) {
-                const f32x2_t x = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, o2, so, 0));
+                const f32x2_t x = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, o2, so, AUX));
                 v[r][NT1] = x[0]; v[r][NT1 + 1] = x[1];
             }
             if constexpr (W2 == 4) {
-                const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, o2, so, 0));
+                const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, o2, so, AUX));
 #pragma unroll
                 for (int t = 0; t < 4; ++t) v[r][NT1 + t] = x[t];
             }

@@ -12,7 +12,13 @@ from broadcast_gemm_amd.inputs import CONFIG_BY_NAME, CONFIGS, bf16_bits_to_f32,
 VARIANTS = ["S0", "S1", "S2", "S3", "S4"]
 ATOL, RTOL = 1e-3, 1.6e-2        # |Y_gpu - Y_ref| <= ATOL + RTOL*|Y_ref|  (bf16 in, fp32 accumulate)
 # Candidates the oracle evaluates one by one at the largest configuration.
-SAMPLED_ROWS = {"extreme-10000to1": [0, 1, 2, 4999, 9998, 9999, 10000, 10001, 15000, 19997, 19998, 19999]}
+# At 10000:1 (two users of 10000 candidates): both ends of each user's run and of the batch,
+# the run boundary, the middle, and a seeded spread between them -- several hundred candidates,
+# every M row (all row chunks of a candidate) and every column of each.
+SAMPLED_ROWS = {"extreme-10000to1": sorted(set(
+    list(range(0, 40)) + list(range(4980, 5020)) + list(range(9960, 10040)) + list(range(14980, 15020))
+    + list(range(19960, 20000))
+    + [int(r) for r in np.random.default_rng(20000).choice(20000, 200, replace=False)]))}
 
 
 def torch():

@@ -117,3 +117,27 @@ def test_fa_map_out_of_range_reported():
         assert plan.check() == bga.IKBO_OK
     finally:
         plan.close()
+
+
+def test_fa_rescale_after_first_block():
+    """A key in the last key block whose score exceeds the running maximum by far more than
+    the kernel's 8 (log2) of headroom: O must be rescaled after block 0 (L_kv = 1024, 16
+    key blocks).  Each candidate gets such a key for one of its queries, aligned with it."""
+    import oracle
+    from broadcast_gemm_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits
+    cfg = FaConfig("fa-rescale", 2, 6, 2, 64, 1024, 128, "bf16", "sorted", 64)
+    log("[fa] rescale after block 0")
+    x = make_fa_inputs(cfg)
+    Q = bf16_bits_to_f32(x.Q)
+    K = bf16_bits_to_f32(x.K)
+    for b in range(cfg.B_c):
+        u = int(x.map[b])
+        for h in range(cfg.H):
+            q = (7 * b + h) % cfg.L_q
+            # score = |Q|^2 * 1.5 / sqrt(128): about 17 against a running maximum near 4
+            K[u, h, cfg.L_kv - 1 - 3 * b - h] = 1.5 * Q[b, h, q]
+    x.K = f32_to_bf16_bits(K)
+    O = gpu_fa(x)
+    ref = oracle.fa_f64(x.Q, x.K, x.V, x.map)
+    assert_close(O, ref, "fa rescale", oracle.fa_weight_bound(x.Q, x.K, x.V, x.map))
+    assert np.all(np.isfinite(O))

@@ -141,6 +141,36 @@ def test_variants_identical_on_repeat_and_resize(variant):
         plan.close()
 
 
+@pytest.mark.parametrize("engine", ["rows", "stream"])
+def test_s4_alternating_inputs_every_element(engine, monkeypatch):
+    """One one-launch (S4) plan at the 70:1 workload fed two input sets in turn, A, B, A, B:
+    every element of every output against the oracle, and the repeats bit-identical.  A
+    candidate that read a user partial left by the previous forward (a stale flag or a stale
+    cache line) would carry the other set's user term and fail."""
+    import dataclasses
+    import oracle
+    monkeypatch.setenv("IKBO_STREAM", "1" if engine == "stream" else "0")
+    base = CONFIG_BY_NAME["default-70to1"]
+    xa = cached_inputs("default-70to1")
+    xb = make_inputs(dataclasses.replace(base, seed=base.seed + 101))
+    ref_a, _ = cached_oracle("default-70to1")
+    ref_b = oracle.lce_f64(xb.U, xb.C, xb.map, xb.W_u, xb.W_c)
+    plan = bga.LcePlan(base.B_u, base.B_c, base.K_u, base.K_c, base.M, base.D, dtype="bf16", variant="S4")
+    try:
+        assert plan.info()["engine"] == engine
+        outs = []
+        for k, (x, ref) in enumerate([(xa, ref_a), (xb, ref_b), (xa, ref_a), (xb, ref_b)]):
+            log(f"[abab] engine={engine} forward {k} set {'AB'[k % 2]}")
+            Y = run(x, "S4", plan=plan)
+            assert_close(to_f64(Y), ref, f"S4/{engine} forward {k}")
+            outs.append(Y)
+        t = torch()
+        assert t.equal(outs[0].view(t.int16), outs[2].view(t.int16))
+        assert t.equal(outs[1].view(t.int16), outs[3].view(t.int16))
+    finally:
+        plan.close()
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_zero_candidates_is_a_noop(variant):
     cfg = CONFIG_BY_NAME["tiny"]

@@ -1,0 +1,246 @@
+"""CPU mirrors of the static schedules of the persistent kernels, checked for coverage:
+every user unit / user tile and every candidate unit (or each of its row-block sub-units)
+is taken by exactly one wave, over grids and work counts around the configurations' own.
+Each mirror restates the kernel's schedule expressions; the test first checks that those
+expressions still stand in the kernel source, so a change there must be mirrored here."""
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "broadcast_gemm_amd", "csrc")
+
+
+def _src(name):
+    with open(os.path.join(CSRC, name)) as f:
+        return " ".join(f.read().split())
+
+
+# ---- row-tile engine (lce_rows.hip) ----
+
+ROWS_LINES = [
+    "const int nuw = both ? imin_t(shared ? (a.n_user + wpb - 1) / wpb * wpb : a.n_user, n_waves) : 0;",
+    "const int V = n_waves - nuw;",
+    "const int wr = n_waves - 1 - w;",
+    "const int r_full = a.n_cand >= V ? 1 + (a.n_cand - V) / n_waves : 0;",
+    "const int N_full = r_full > 0 ? V + (r_full - 1) * n_waves : 0;",
+    "const int n_sub = (a.n_cand - N_full) * MB;",
+    "const int c = w >= nuw ? (k == 0 ? wr : V + (k - 1) * n_waves + wr) : V + k * n_waves + wr;",
+    "for (int sidx = wr; sidx < n_sub;) {",
+]
+
+
+def test_rows_mirror_matches_kernel_source():
+    src = _src("lce_rows.hip")
+    for line in ROWS_LINES:
+        assert " ".join(line.split()) in src, line
+
+
+def rows_schedule(n_waves, wpb, n_user, n_cand, MB, lds_shared):
+    """Per wave: (user units, full candidate units, sub-units), in the order taken."""
+    both = n_user > 0 and n_cand > 0
+    shared = both and lds_shared
+    nuw = min(-(-n_user // wpb) * wpb if shared else n_user, n_waves) if both else 0
+    V = n_waves - nuw
+    r_full = 1 + (n_cand - V) // n_waves if n_cand >= V else 0
+    N_full = V + (r_full - 1) * n_waves if r_full > 0 else 0
+    n_sub = (n_cand - N_full) * MB
+    out = []
+    for w in range(n_waves):
+        wr = n_waves - 1 - w
+        users = list(range(w, n_user, n_waves))
+        cands, k = [], 0
+        while True:
+            c = (wr if k == 0 else V + (k - 1) * n_waves + wr) if w >= nuw else V + k * n_waves + wr
+            if c >= N_full:
+                break
+            cands.append(c)
+            k += 1
+        subs = list(range(wr, n_sub, n_waves))
+        out.append((users, cands, subs))
+    return out, N_full, nuw, V
+
+
+ROWS_CASES = [(n_waves, wpb, n_user, n_cand, MB, shared)
+              for n_waves in (4, 64, 1020, 1024)
+              for wpb in (1, 4)
+              for n_user in (0, 1, 3, 90, 1000)
+              for n_cand in (0, 1, 5, 700, 1024, 2048, 3000)
+              for MB in (1, 3, 6)
+              for shared in (False, True)
+              if not (n_user > 0 and n_cand > 0 and n_user > n_waves)]   # the host's guarantee
+
+
+@pytest.mark.parametrize("case", ROWS_CASES[::7] + ROWS_CASES[-5:])
+def test_rows_schedule_covers_every_unit_once(case):
+    n_waves, wpb, n_user, n_cand, MB, shared = case
+    sched, N_full, nuw, V = rows_schedule(*case)
+    users = sorted(t for u, _, _ in sched for t in u)
+    assert users == list(range(n_user))
+    fulls = sorted(c for _, cs, _ in sched for c in cs)
+    assert fulls == list(range(N_full))
+    subs = sorted(s for _, _, ss in sched for s in ss)
+    assert subs == list(range((n_cand - N_full) * MB))
+    if n_user > 0 and n_cand > 0:
+        for w, (u, cs, _) in enumerate(sched):
+            assert len(u) <= 1 and (not u or u[0] == w)        # a user unit is a wave's first unit
+            if cs and cs[0] < V:
+                assert w >= nuw                                  # round 0 skips the user waves
+
+
+# ---- streaming engine (lce_stream.hip) ----
+
+STREAM_LINES = [
+    "const int nb = (int)gridDim.x, x = bid & 7, q = nb >> 3, r = nb & 7;",
+    "bid = x * q + imin_t(x, r) + (bid >> 3);",
+    "const int w = (int)__builtin_amdgcn_readfirstlane(bid * (kStreamBlock / 64) + wv);",
+    "const int n_own = (int)gridDim.x * tw;",
+    "int t = wv < tw ? (int)__builtin_amdgcn_readfirstlane(bid * tw + wv) : a.n_utiles;",
+    "t = (int)__builtin_amdgcn_readfirstlane(t + n_own);",
+    "const int un = uu + n_waves;",
+]
+
+
+def test_stream_mirror_matches_kernel_source():
+    src = _src("lce_stream.hip")
+    for line in STREAM_LINES:
+        assert " ".join(line.split()) in src, line
+
+
+def xcd_order(bid, nb):
+    x, q, r = bid & 7, nb >> 3, nb & 7
+    return x * q + min(x, r) + (bid >> 3)
+
+
+@pytest.mark.parametrize("nb", list(range(1, 70)) + [127, 128, 129, 255, 256, 257, 511, 512, 1000])
+def test_stream_xcd_order_is_a_bijection(nb):
+    got = sorted(xcd_order(b, nb) for b in range(nb))
+    assert got == list(range(nb))
+    # consecutive schedule numbers sit on one XCD (blockIdx % 8) except at the XCD boundaries
+    inv = {xcd_order(b, nb): b for b in range(nb)}
+    changes = sum(1 for k in range(1, nb) if inv[k] % 8 != inv[k - 1] % 8)
+    assert changes <= 7
+
+
+@pytest.mark.parametrize("nb,tw,n_units,n_tiles", [
+    (256, 4, 1024, 900), (256, 4, 400, 3540), (256, 2, 20000, 128), (18, 4, 70, 72), (81, 4, 70, 324),
+    (64, 1, 256, 1560), (1, 4, 3, 5), (7, 2, 0, 33), (5, 4, 17, 0)])
+def test_stream_schedule_covers_every_unit_and_tile_once(nb, tw, n_units, n_tiles):
+    n_waves = nb * 4
+    n_own = nb * tw
+    units, tiles = [], []
+    for blk in range(nb):
+        bid = xcd_order(blk, nb)
+        for wv in range(4):
+            w = bid * 4 + wv
+            units += list(range(w, n_units, n_waves))
+            if wv < tw:
+                tiles += list(range(bid * tw + wv, n_tiles, n_own))
+    assert sorted(units) == list(range(n_units))
+    assert sorted(tiles) == list(range(n_tiles))
+
+
+# ---- streaming engine: lane offsets of the loads, the epilogue and the LDS reads ----
+
+STREAM_TILE_LINES = [
+    "off_m = ((8 * g) * DCOV + 8 * j) * 2;",
+    "off_q = ((8 * g + 2 * (j & 3)) * DCOV + 128 * N8 + 8 * (j >> 2)) * 2;",
+    "raw[S][r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off_m + r * DCOV * 2, so, 0));",
+    "u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off_q + p * DCOV * 2 + 64 * qg, so, 0));",
+    "static __device__ __forceinline__ int main_col(int j) { return 8 * j; }",
+    "static __device__ __forceinline__ int quad_col(int qg, int j) { return 128 * N8 + 32 * qg + 2 * j; }",
+    "pa[mb] = wl + (uint32_t)(mr * K + ks * 32 + 8 * g) * 2;",
+]
+
+LAYOUTS = {32: (0, 1), 64: (0, 2), 128: (1, 0), 160: (1, 1), 192: (1, 2)}
+
+
+def test_stream_tile_mirror_matches_kernel_source():
+    src = _src("lce_stream.h")
+    for line in STREAM_TILE_LINES:
+        assert " ".join(line.split()) in src, line
+
+
+@pytest.mark.parametrize("D", sorted(LAYOUTS))
+def test_stream_step_loads_cover_the_step_once(D):
+    """The 64 lanes' 16-byte loads of one K step tile its 32 rows x D columns exactly once,
+    each load inside one row."""
+    N8, NQ = LAYOUTS[D]
+    DCOV = 128 * N8 + 32 * NQ
+    assert DCOV == D
+    seen = [0] * (32 * D * 2 // 16)
+    for lane in range(64):
+        g, j = lane >> 4, lane & 15
+        off_m = ((8 * g) * DCOV + 8 * j) * 2
+        off_q = ((8 * g + 2 * (j & 3)) * DCOV + 128 * N8 + 8 * (j >> 2)) * 2
+        offs = [off_m + r * DCOV * 2 for r in range(8 * N8)]
+        offs += [off_q + p * DCOV * 2 + 64 * qg for qg in range(NQ) for p in range(2)]
+        for o in offs:
+            assert o % 16 == 0 and 0 <= o and o + 16 <= 32 * D * 2
+            assert o // (D * 2) == (o + 15) // (D * 2)          # inside one row
+            seen[o // 16] += 1
+    assert all(c == 1 for c in seen)
+
+
+@pytest.mark.parametrize("D", sorted(LAYOUTS))
+def test_stream_epilogue_writes_each_element_once(D):
+    """Lane (g, j) holds rows 4g + i of a 16-row block: 8 main columns from main_col(j), and two
+    columns from quad_col(qg, j) per quad group; together every element once."""
+    N8, NQ = LAYOUTS[D]
+    seen = {}
+    for lane in range(64):
+        g, j = lane >> 4, lane & 15
+        for i in range(4):
+            r = 4 * g + i
+            if N8:
+                for t in range(8):
+                    seen[(r, 8 * j + t)] = seen.get((r, 8 * j + t), 0) + 1
+            for qg in range(NQ):
+                for t in range(2):
+                    c = 128 * N8 + 32 * qg + 2 * j + t
+                    seen[(r, c)] = seen.get((r, c), 0) + 1
+    assert sorted(seen) == [(r, c) for r in range(16) for c in range(D)]
+    assert set(seen.values()) == {1}
+
+
+def stream_w_bytes(M, K):
+    nchunk = ((M * K + 7) // 8 + 63) // 64
+    need = (M * K + 40) * 2
+    b = max(nchunk * 1024, need)
+    return (b + 1023) // 1024 * 1024
+
+
+@pytest.mark.parametrize("M,K", [(96, 197), (128, 251), (48, 77), (1, 1), (17, 33), (112, 32), (96, 301)])
+def test_stream_lds_reads_stay_in_their_copy(M, K):
+    """A-operand reads of the W copy (16 bytes at row mr, element 32ks + 8g) and the DMA copy
+    of the matrix (1 KB chunks) stay inside the bytes reserved for it."""
+    n_ks = -(-K // 32)
+    cap = stream_w_bytes(M, K)
+    for mr in range(M):
+        for ks in range(n_ks):
+            for g in range(4):
+                lo = (mr * K + ks * 32 + 8 * g) * 2
+                assert 0 <= lo and lo + 16 <= cap
+    nblk = (M * K + 7) // 8
+    nchunk = (nblk + 63) // 64
+    assert nchunk * 1024 <= cap
+
+
+@pytest.mark.parametrize("K_u", [1, 31, 32, 40, 120, 301, 509])
+def test_stream_user_tile_reads_stay_in_the_region(K_u):
+    """A user tile's reads: B from the U slice (rows 32 bytes apart, n_ks_u KB) and A from the
+    16-row W_u copy after it; both inside the owner's region (n_ks_u KB + the W_u copy)."""
+    n_ks_u = -(-K_u // 32)
+    slice_bytes = n_ks_u * 1024
+    region = slice_bytes + stream_w_bytes(16, K_u)
+    for lane in range(64):
+        g, j = lane >> 4, lane & 15
+        pb = 256 * g + 2 * j
+        pa = slice_bytes + (j * K_u + 8 * g) * 2
+        for s in range(n_ks_u):
+            for r in range(8):
+                o = pb + 1024 * s + 32 * r
+                assert o + 2 <= slice_bytes
+            assert pa + 64 * s + 16 <= region
+    # the DMA of the slice (n_ks_u chunks) and of the W_u rows (ceil(32 K_u / 1024) chunks)
+    assert slice_bytes + -(-32 * K_u // 1024) * 1024 <= region
