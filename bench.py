@@ -177,6 +177,34 @@ def run_traffic(args) -> int:
     return 0
 
 
+def run_counters(args) -> int:
+    """Per-kernel means of every counter found in rocprofv3 --pmc output directories (no GPU):
+    one JSON line per kernel (name, grid) with the mean value per dispatch of each counter."""
+    import csv
+    import glob
+    table = {}
+    for d in args.counters:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as fh:
+                for r in csv.DictReader(fh):
+                    name = r.get("Kernel_Name", "")
+                    if "__amd_rocclr" in name:
+                        continue
+                    key = (name, r.get("Grid_Size"))
+                    table.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not table:
+        raise SystemExit("no counter rows found")
+    for (name, grid), ctrs in sorted(table.items()):
+        out = {"kernel": name, "grid": grid,
+               "counters": {c: round(sum(v) / len(v), 3) for c, v in sorted(ctrs.items())},
+               "dispatches": {c: len(v) for c, v in sorted(ctrs.items())}}
+        h, m = out["counters"].get("TCC_HIT_sum"), out["counters"].get("TCC_MISS_sum")
+        if h is not None and m is not None and h + m > 0:
+            out["counters"]["L2_hit_percent"] = round(100.0 * h / (h + m), 2)
+        print(json.dumps(out), flush=True)
+    return 0
+
+
 def run_rewrite(args, cfg, sets) -> int:
     """An unmodified model's materialised broadcast (cat of U[map] and C, then one batched
     matmul with [W_u | W_c], in torch on the GPU) against the same module after the
@@ -637,7 +665,10 @@ def main() -> int:
     ap.add_argument("--rotate-mb", type=int, default=1100, help="total size of rotated buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--mode", default="lce", choices=["lce", "copy", "traffic", "rewrite", "rewrite-fa", "backward", "fa", "fa-fused"])
+    ap.add_argument("--mode", default="lce", choices=["lce", "copy", "traffic", "counters", "rewrite", "rewrite-fa", "backward",
+                                                      "fa", "fa-fused"])
+    ap.add_argument("--counters", nargs="+", metavar="PMC_DIR",
+                    help="--mode counters: rocprofv3 --pmc output directories")
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="--mode traffic: rocprofv3 --pmc output directories")
@@ -646,6 +677,8 @@ def main() -> int:
                     help="--mode traffic: sum every launch of one forward (multi-launch ladder stages)")
     ap.add_argument("--copy-match", default="copyBuffer")
     args = ap.parse_args()
+    if args.mode == "counters":
+        return run_counters(args)
     if args.mode == "traffic":
         return run_traffic(args)
 
