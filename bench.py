@@ -45,7 +45,8 @@ def dominant_kernel(info: dict):
         return {"S3": ("lce_stream_kernel (candidate)", 2),
                 "S4": ("lce_stream_kernel (user tiles + candidates, one launch)", 1)}.get(v, ("whole forward", 0))
     if eng == "rows":
-        return {"S0": ("lce_rows_kernel (materialised X)", 3), "S2": ("lce_rows_kernel (candidate)", 4),
+        return {"S0": ("lce_rows_kernel (materialised X)", 3), "S1": ("lce_rows_kernel (candidate, 4-byte loads)", 4),
+                "S2": ("lce_rows_kernel (candidate)", 4),
                 "S3": ("lce_rows_kernel (candidate)", 2),
                 "S4": ("lce_rows_kernel (user + candidate, one launch)", 1)}.get(v, ("whole forward", 0))
     return {"S4": ("lce_fused_kernel", 2)}.get(v, ("whole forward", 0))

@@ -219,7 +219,7 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
 
     // ---- engine choice ----
     p->engine = ENGINE_FLAT;
-    if (dtype == IKBO_DTYPE_BF16 && variant != IKBO_S1_DECOMPOSED && rows_supported(D)) {
+    if (dtype == IKBO_DTYPE_BF16 && rows_supported(D)) {
         const int mb = choose_mb(n_mblocks, rows_max_mb(D));
         const int mpad = ceil_div(n_mblocks, mb) * mb * 16;
         // The staged projections (as is, plus slack) must fit one workgroup's LDS.
@@ -429,6 +429,7 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
         r.M = M; r.M_pad = p->M_pad; r.K_u = K_u;
         r.K_wc = variant == IKBO_S0_MATERIALISED ? p->ldw_cat : K_c;
         const int epi = variant == IKBO_S0_MATERIALISED ? EPI_STORE_T
+                        : variant == IKBO_S1_DECOMPOSED  ? EPI_STORE_F32_NARROW
                         : variant == IKBO_S2_ALIGNED     ? EPI_STORE_F32
                                                          : EPI_ADD_USER;
         auto bpc = [&](int nu, int nc) {
@@ -580,13 +581,16 @@ int forward_rows(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t 
             if ((e = rows_launch(p, EPI_STORE_T, c, p->bpc_cand, s)) != hipSuccess) return hip_fail(e, "rows gemm");
             break;
         }
+        case IKBO_S1_DECOMPOSED:
         case IKBO_S2_ALIGNED: {
+            // S1 and S2 differ only in the width of the activation loads (4 against 16 bytes).
+            const int epi = p->variant == IKBO_S1_DECOMPOSED ? EPI_STORE_F32_NARROW : EPI_STORE_F32;
             RowArgs u = a;
             u.n_user = n_user; u.n_cand = 0;
-            if ((e = rows_launch(p, EPI_STORE_F32, u, p->bpc_user, s)) != hipSuccess) return hip_fail(e, "user gemm");
+            if ((e = rows_launch(p, epi, u, p->bpc_user, s)) != hipSuccess) return hip_fail(e, "user gemm");
             RowArgs c = a;
             c.n_user = 0; c.n_cand = n_cand; c.out = p->P_c;
-            if ((e = rows_launch(p, EPI_STORE_F32, c, p->bpc_cand, s)) != hipSuccess) return hip_fail(e, "cand gemm");
+            if ((e = rows_launch(p, epi, c, p->bpc_cand, s)) != hipSuccess) return hip_fail(e, "cand gemm");
             if ((e = launch_bcast_rows(p->P_u, map, p->P_b, B_u, B_c, M, D, p->err, s)) != hipSuccess)
                 return hip_fail(e, "bcast");
             if ((e = launch_add_cast(dt, p->P_c, p->P_b, Y, (long long)B_c * M * D, s)) != hipSuccess)

@@ -14,7 +14,8 @@ enum DType { DT_BF16 = 0, DT_F32 = 1 };
 enum Epi {
     EPI_STORE_F32 = 0,  // out = acc (float32), e.g. the user partial P_u or the candidate partial P_c
     EPI_ADD_USER = 1,   // out = T(acc + P_u[map[b]])  (gather-add epilogue)
-    EPI_STORE_T = 2     // out = T(acc)
+    EPI_STORE_T = 2,    // out = T(acc)
+    EPI_STORE_F32_NARROW = 3   // as EPI_STORE_F32, every activation load 4 bytes wide (row-tile engine)
 };
 
 // Device error bits (OR-ed into the plan's error word).

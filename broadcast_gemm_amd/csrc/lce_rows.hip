@@ -75,9 +75,9 @@ __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)
 // load of a block can be in flight at once.  The lane's base offset covers its
 // row group and column slot; the row within the block travels in the scalar
 // offset.
-template <int MB, int N8, int W2, int NS, int EPI>
+template <int MB, int N8, int W2, int NS, int EPI, bool NARROW = false>
 struct Rows {
-    using Tile = RowTile<MB, N8, W2, NS>;
+    using Tile = RowTile<MB, N8, W2, NS, NARROW>;
     static constexpr int NT1 = Tile::NT1;
     static constexpr int NT = Tile::NT;   // output columns a lane owns in one row
     static constexpr int D = Tile::DCOV;
@@ -248,9 +248,12 @@ __device__ __forceinline__ void wait_flag(const RowArgs &a, const uint32_t *f, i
 
 constexpr int kRing = 4;   // K steps in the register ring (three in flight while one multiplies)
 
-template <int MB, int N8, int W2, int EPI>
+template <int MB, int N8, int W2, int EPI_IN>
 __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
-    using R = Rows<MB, N8, W2, kRing, EPI>;
+    // EPI_STORE_F32_NARROW is EPI_STORE_F32 with 4-byte activation loads.
+    constexpr bool NARROW = EPI_IN == EPI_STORE_F32_NARROW;
+    constexpr int EPI = NARROW ? (int)EPI_STORE_F32 : EPI_IN;
+    using R = Rows<MB, N8, W2, kRing, EPI, NARROW>;
     using Tile = typename R::Tile;
 
     const int wpb = (int)(blockDim.x >> 6);
@@ -534,6 +537,7 @@ rows_kernel_t pick(int epi, int D, int mb) {
         case EPI_STORE_F32: return pick_layout<EPI_STORE_F32>(D, mb);
         case EPI_ADD_USER: return pick_layout<EPI_ADD_USER>(D, mb);
         case EPI_STORE_T: return pick_layout<EPI_STORE_T>(D, mb);
+        case EPI_STORE_F32_NARROW: return pick_layout<EPI_STORE_F32_NARROW>(D, mb);
     }
     return nullptr;
 }

@@ -86,7 +86,9 @@ __host__ __device__ inline int lds_w_elems(int M, int K) { return (M * K + 7) / 
 
 // ---- the tile ---------------------------------------------------------------------------
 
-template <int MB, int N8, int W2, int NS>
+// NARROW: the same data, but every activation load 4 bytes wide (the unaligned-load stage of
+// the ladder, for comparison on one engine).
+template <int MB, int N8, int W2, int NS, bool NARROW = false>
 struct RowTile {
     static constexpr int NT1 = N8 ? 8 : 0;
     static constexpr int NT = NT1 + W2;
@@ -116,13 +118,27 @@ struct RowTile {
         const int so = ks * 32 * DCOV * 2;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            if constexpr (N8 != 0)
-                r1[S][r].v = __builtin_bit_cast(
-                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off1 + r * DCOV * 2, so, 0));
+            if constexpr (N8 != 0) {
+                if constexpr (NARROW) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        r1[S][r].v[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, off1 + r * DCOV * 2 + 4 * q, so, 0);
+                } else {
+                    r1[S][r].v = __builtin_bit_cast(
+                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off1 + r * DCOV * 2, so, 0));
+                }
+            }
             if constexpr (W2 == 2) r2[S][r].v = __builtin_amdgcn_raw_buffer_load_b32(rs, off2 + r * DCOV * 2, so, 0);
-            if constexpr (W2 == 4)
-                r2[S][r].v = __builtin_bit_cast(
-                    u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off2 + r * DCOV * 2, so, 0));
+            if constexpr (W2 == 4) {
+                if constexpr (NARROW) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        r2[S][r].v[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, off2 + r * DCOV * 2 + 4 * q, so, 0);
+                } else {
+                    r2[S][r].v = __builtin_bit_cast(
+                        u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off2 + r * DCOV * 2, so, 0));
+                }
+            }
         }
     }
 
