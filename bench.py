@@ -121,11 +121,12 @@ def _mean_kib(d: str, counter: str, match: str) -> tuple:
 
 def _forward_kib(d: str, counter: str) -> tuple:
     """Per-forward sum over the launches of a forward: the mean of each distinct (kernel, grid)
-    that is not a runtime copy or fill (each appears once per forward in every ladder stage)."""
+    of the library (each appears once per forward in every ladder stage); the runtime's copies
+    and fills and torch's input generation are left out."""
     groups = {}
     for r in _counter_rows(d, counter):
         name = r.get("Kernel_Name", "")
-        if "__amd_rocclr" in name:
+        if "ikbo::" not in name:
             continue
         groups.setdefault((name, r.get("Grid_Size")), []).append(float(r["Counter_Value"]))
     if not groups:
@@ -189,7 +190,7 @@ def run_counters(args) -> int:
             with open(path) as fh:
                 for r in csv.DictReader(fh):
                     name = r.get("Kernel_Name", "")
-                    if "__amd_rocclr" in name:
+                    if "ikbo::" not in name:
                         continue
                     key = (name, r.get("Grid_Size"))
                     table.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))

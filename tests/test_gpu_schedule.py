@@ -2,7 +2,8 @@
 edge cases: partial last rounds split into row-block sub-units (with a ragged last
 row chunk), waves left with a single candidate unit, more user units than waves
 (the one-launch stage falls back to two launches), every column layout of the
-row-tile engine (D = 32, 64, 128, 160, 192), and projections too large to sit in
+row-tile engine (D = 32, 64, 128, 160, 192) with both activation load widths (S1
+loads 4 bytes per lane, the other stages 16), and projections too large to sit in
 LDS together (the one-launch stage then holds them one after the other).
 
 Bar: per element |Y_gpu - Y_ref| <= 1e-3 + 1.6e-2*|Y_ref|, as in test_gpu_parity.
@@ -40,7 +41,7 @@ SHAPES = [
 def _cases():
     for sh in SHAPES:
         sid = f"{sh[0]}x{sh[1]}-K{sh[2]}_{sh[3]}-M{sh[4]}-D{sh[5]}-{sh[6]}"
-        for v in ["S0", "S2", "S3", "S4"]:
+        for v in ["S0", "S1", "S2", "S3", "S4"]:
             # S0's packed [W_u | W_c] (M x (K_u + K_c)) must fit LDS for the rows engine.
             if v == "S0" and sh[4] * (sh[2] + sh[3]) * 2 > 150 * 1024:
                 continue
