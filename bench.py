@@ -32,6 +32,7 @@ METRIC = "IKBO-LCE fwd µs + TFLOP/s & HBM GB/s at B_c=1024, 70:1; % of roofline
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 KERNEL_SOURCES = ["broadcast_gemm_amd/csrc/lce_stream.hip", "broadcast_gemm_amd/csrc/lce_stream.h",
+                  "broadcast_gemm_amd/csrc/lce_sync.h",
                   "broadcast_gemm_amd/csrc/lce_rows.hip", "broadcast_gemm_amd/csrc/lce_rowtile.h",
                   "broadcast_gemm_amd/csrc/lce_fused.hip", "broadcast_gemm_amd/csrc/lce_tile.h",
                   "broadcast_gemm_amd/csrc/lce_device.h", "broadcast_gemm_amd/csrc/lce_kernels.hip",

@@ -5,7 +5,8 @@
 //   stream -- one wave per (batch entry, M chunk of up to all M rows), all D columns, every
 //             activation load 16 bytes wide, the user product cut into 16x16 tiles spread
 //             over every wave (lce_stream.hip); bf16 with D in {32, 64, 128, 160, 192}: the
-//             stages with the gather-add epilogue (S3, S4);
+//             two-launch gather-add stage S3 when its units fit one round of the waves, and
+//             either gather-add stage on request;
 //   rows   -- one wave per (batch entry, M chunk), all D columns of the entry,
 //             projection staged in LDS (lce_rows.hip); bf16 with D in
 //             {32, 64, 128, 160, 192} when the staged projection fits in LDS;
@@ -250,8 +251,8 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     }
 
     // ---- the streaming engine takes the stages with the gather-add epilogue ----
-    // By default the two-launch stage; IKBO_STREAM=1 puts the one-launch stage on it too, 0
-    // keeps both on the row-tile engine.
+    // By default the two-launch stage when its units fit one round; IKBO_STREAM=1 puts both
+    // gather-add stages on it whatever the size, 0 keeps both on the row-tile engine.
     const int stream_env = env_int("IKBO_STREAM", -1);
     const bool stream_wanted = stream_env < 0 ? variant == IKBO_S3_EPILOGUE_FUSED
                                               : (stream_env != 0 && (variant == IKBO_S3_EPILOGUE_FUSED ||
@@ -267,6 +268,10 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
         const size_t l_c = lds_of(1, 0, 4), l_u = lds_of(0, 1, 4);
         const int mb = stream_choose_mb(n_mblocks, stream_max_mb(D), max_B_c, p->n_cu * (kStreamBlock / 64));
         const int nmc = ceil_div(n_mblocks, mb);
+        // By default the two-launch stage takes this engine only when its units fit one round
+        // (at most one per wave); with more, the rows engine's sub-unit tail is faster (measured
+        // at 10:1, 4096 random and 10000:1).
+        const bool one_round = (long long)max_B_c * nmc <= (long long)p->n_cu * (kStreamBlock / 64);
         const int bc = l_c <= (size_t)max_lds ? stream_blocks_per_cu(EPI_ADD_USER, D, mb, l_c) : 0;
         const int bu = l_u <= (size_t)max_lds ? stream_blocks_per_cu(EPI_ADD_USER, D, mb, l_u) : 0;
         // One launch: as many tile-owning waves per workgroup as the LDS holds next to W_c.
@@ -277,7 +282,7 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
             if (bf >= 1) break;
         }
         // Byte offsets within one fp32 [M][D] matrix and one [K][D] matrix are 32-bit.
-        if (bc >= 1 && bu >= 1 && (long long)M * D * 4 < (1LL << 31) &&
+        if ((stream_env >= 0 || one_round) && bc >= 1 && bu >= 1 && (long long)M * D * 4 < (1LL << 31) &&
             (long long)std::max(K_u, K_c) * D * 2 < (1LL << 31)) {
             p->engine = ENGINE_STREAM;
             p->st_mb = mb;
