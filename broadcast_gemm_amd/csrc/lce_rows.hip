@@ -312,6 +312,10 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         return c < N_full ? uniform_rsrc(a.C + (size_t)(c / n_mc) * a.K_c * D, a.K_c * D * 2) : sub_rsrc(wr);
     };
 
+    // The map through scalar loads (wave-uniform indices): a vector load would be waited for
+    // together with every load the wave has in flight, the ring's prefetch of the unit included.
+    const __attribute__((address_space(4))) int32_t *map_s = (const __attribute__((address_space(4))) int32_t *)a.map;
+
     Tile T;
     T.init(g, j);
     int t = w;                     // current user unit
@@ -414,8 +418,8 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
             // wait for a user product comes after two units' worth of reads.
             const int c1 = cand_of(1), c2 = cand_of(2);
             const __amdgpu_buffer_rsrc_t rs1 = cand_rsrc(c1), rs2 = cand_rsrc(c2);
-            const int u0 = (int)__builtin_amdgcn_readfirstlane(a.map[c / n_mc]);
-            const int u1 = c1 < N_full ? (int)__builtin_amdgcn_readfirstlane(a.map[c1 / n_mc]) : 0;
+            const int u0 = (int)__builtin_amdgcn_readfirstlane(map_s[c / n_mc]);
+            const int u1 = c1 < N_full ? (int)__builtin_amdgcn_readfirstlane(map_s[c1 / n_mc]) : 0;
             T.zero();
             T.run(rs, rs1, a.n_ks_c, wl_c, a.K_wc, a.M, (c % n_mc) * MB * 16, g, j);
             const Tile T0 = T;
@@ -442,7 +446,7 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         if constexpr (EPI == EPI_ADD_USER) {
             // Later units start their accumulators from the rows of P_u[map[b]] (in place by
             // then: a launch without user units, or after the wave's first two units).
-            const int u = (int)__builtin_amdgcn_readfirstlane(a.map[b]);
+            const int u = (int)__builtin_amdgcn_readfirstlane(map_s[b]);
             const bool valid = u >= 0 && u < a.B_u;
             if (valid) {
                 if (a.wait_flags) wait_user(u, mc);
@@ -478,7 +482,7 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         const size_t obase = (size_t)b * a.M * D;
         T.zero();
         if constexpr (EPI == EPI_ADD_USER) {
-            const int u = (int)__builtin_amdgcn_readfirstlane(a.map[b]);
+            const int u = (int)__builtin_amdgcn_readfirstlane(map_s[b]);
             const bool valid = u >= 0 && u < a.B_u;
             if (valid) {
                 if (a.wait_flags) wait_user(u, mc, blk, 1);

@@ -225,6 +225,10 @@ __global__ void __launch_bounds__(kStreamBlock, 1) lce_stream_kernel(StreamArgs 
         if (lane == 0) st_flag(&a.flags[t], a.epoch);
     };
 
+    // The map through scalar loads (wave-uniform indices): a vector load would be waited for
+    // together with every load the wave has in flight, the next unit's opening steps included.
+    const __attribute__((address_space(4))) int32_t *map_s = (const __attribute__((address_space(4))) int32_t *)a.map;
+
     Tile T;
     T.init(g, j);
     int uu = w;
@@ -295,7 +299,7 @@ __global__ void __launch_bounds__(kStreamBlock, 1) lce_stream_kernel(StreamArgs 
             }
         });
         if constexpr (EPI == EPI_ADD_USER) {
-            const int u = (int)__builtin_amdgcn_readfirstlane(a.map[b]);
+            const int u = (int)__builtin_amdgcn_readfirstlane(map_s[b]);
             if (u < 0 || u >= a.B_u) {
                 if (lane == 0) atomicOr(a.err, ERRBIT_MAP);
             } else {
