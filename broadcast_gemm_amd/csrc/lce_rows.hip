@@ -168,23 +168,6 @@ struct Rows {
             for (int t = 0; t < NT; ++t) v[r][t] = in_vgpr(T.acc[mb][t][r]);
     }
 
-    // Accumulators (first MBX row blocks) = the tile's rows of an fp32 [M][D] matrix.
-    template <int MBX = MB>
-    static __device__ __forceinline__ void init_from(const RowArgs &a, Tile &T, const float *base, int mrow0, int g,
-                                                     int j) {
-        const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(base, a.M * D * 4);
-        const int o1 = off1(mrow0, g, j, 4), o2 = off2(mrow0, g, j, 4);
-#pragma unroll
-        for (int mb = 0; mb < MBX; ++mb) {
-            float v[4][NT];
-            load_block(rs, o1, o2, mb, v);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int t = 0; t < NT; ++t) T.acc[mb][t][r] = v[r][t];
-        }
-    }
-
     // The first MBX row blocks of the tile into an fp32 [M][D] matrix.
     template <int AUX, int MBX = MB>
     static __device__ __forceinline__ void store_f32(const RowArgs &a, const Tile &T, float *base, int mrow0, int g,
@@ -399,6 +382,19 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         }
         asm volatile("" ::: "memory");   // P_u loads stay after the flags
     };
+    // Every user block of the launch published: later epilogues need not poll.  Checked once, with
+    // one read of every flag, where the wave has just waited for its loads anyway.
+    bool all_ready = !a.wait_flags;
+    auto check_all = [&]() {
+        const int nf = a.B_u * n_mb;
+        bool ok = true;
+        for (int i0 = 0; i0 < nf; i0 += 64) {
+            const int i = i0 + lane;
+            const uint32_t v = i < nf ? ld_flag(&a.flags[2 + i]) : a.epoch;
+            ok = ok && __ballot(v != a.epoch) == 0;
+        }
+        all_ready = ok;
+    };
     // Gather-add epilogue after waiting for the user flag (bounded): Y = tile + P_u[map[b]].
     auto add_user_store = [&](const Tile &X, int cc, int u) {
         const int mc = cc % n_mc;
@@ -407,7 +403,7 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
             if (lane == 0) atomicOr(a.err, ERRBIT_MAP);
             return;
         }
-        if (a.wait_flags) wait_user(u, mc);
+        if (!all_ready) wait_user(u, mc);
         R::template store_bf16<true>(a, X, static_cast<uint16_t *>(a.out) + (size_t)b * a.M * D,
                                      a.P_u + (size_t)u * a.M * D, mc * MB * 16, g, j);
     };
@@ -427,6 +423,12 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
                 T.zero();
                 T.run(rs1, rs2, a.n_ks_c, wl_c, a.K_wc, a.M, (c1 % n_mc) * MB * 16, g, j);
             }
+            if (u0 >= 0 && u0 < a.B_u && (c2 < N_full || wr < n_sub)) {
+                // A wave with units after the pair checks every flag once, right after its first
+                // wait (a wave without them has nothing to gain from it).
+                wait_user(u0, c % n_mc);
+                check_all();
+            }
             add_user_store(T0, c, u0);
             if (c1 < N_full) add_user_store(T, c1, u1);
             c = c2;
@@ -444,19 +446,19 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         const size_t obase = (size_t)b * a.M * D;
         T.zero();
         if constexpr (EPI == EPI_ADD_USER) {
-            // Later units start their accumulators from the rows of P_u[map[b]] (in place by
-            // then: a launch without user units, or after the wave's first two units).
+            // The K loop first, then the user rows added in the epilogue: their loads go out while
+            // the ring already holds the next unit's opening steps, so they wait for nothing the
+            // wave would not wait for next anyway (read before the loop, they would be waited for
+            // together with this unit's prefetched steps).
             const int u = (int)__builtin_amdgcn_readfirstlane(map_s[b]);
-            const bool valid = u >= 0 && u < a.B_u;
-            if (valid) {
-                if (a.wait_flags) wait_user(u, mc);
-                R::init_from(a, T, a.P_u + (size_t)u * a.M * D, mrow0, g, j);
-            }
             T.run(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
-            if (valid)
-                R::template store_bf16<false>(a, T, static_cast<uint16_t *>(a.out) + obase, nullptr, mrow0, g, j);
-            else if (lane == 0)
+            if (u >= 0 && u < a.B_u) {
+                if (!all_ready) wait_user(u, mc);
+                R::template store_bf16<true>(a, T, static_cast<uint16_t *>(a.out) + obase,
+                                             a.P_u + (size_t)u * a.M * D, mrow0, g, j);
+            } else if (lane == 0) {
                 atomicOr(a.err, ERRBIT_MAP);
+            }
         } else {
             T.run(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
             if constexpr (EPI == EPI_STORE_F32)
@@ -483,17 +485,14 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         T.zero();
         if constexpr (EPI == EPI_ADD_USER) {
             const int u = (int)__builtin_amdgcn_readfirstlane(map_s[b]);
-            const bool valid = u >= 0 && u < a.B_u;
-            if (valid) {
-                if (a.wait_flags) wait_user(u, mc, blk, 1);
-                R::template init_from<1>(a, T, a.P_u + (size_t)u * a.M * D, mrow0, g, j);
-            }
             T.template run<1>(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
-            if (valid)
-                R::template store_bf16<false, 1>(a, T, static_cast<uint16_t *>(a.out) + obase, nullptr, mrow0, g,
-                                                 j);
-            else if (lane == 0)
+            if (u >= 0 && u < a.B_u) {
+                if (!all_ready) wait_user(u, mc, blk, 1);
+                R::template store_bf16<true, 1>(a, T, static_cast<uint16_t *>(a.out) + obase,
+                                                a.P_u + (size_t)u * a.M * D, mrow0, g, j);
+            } else if (lane == 0) {
                 atomicOr(a.err, ERRBIT_MAP);
+            }
         } else {
             T.template run<1>(rs, rs_next, a.n_ks_c, wl_c, a.K_wc, a.M, mrow0, g, j);
             if constexpr (EPI == EPI_STORE_F32)
