@@ -39,17 +39,12 @@
 
 #include "lce_internal.h"
 #include "lce_rowtile.h"
+#include "lce_sync.h"
 
 namespace ikbo {
 
 namespace {
 
-__device__ __forceinline__ uint32_t ld_flag(const uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_flag(uint32_t *p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 constexpr int kSc1 = 16;   // buffer cache-policy bit sc1: device scope (write through this XCD's L2)
 constexpr int kNt = 2;     // buffer cache-policy bit nt: non-temporal (streaming) stores
 
@@ -273,8 +268,10 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     // Rounds that are complete hold N_full units; the L < T units of a partial last round are
     // split into their MB row blocks (sub-units of 16 rows), spread over the waves in reverse
     // order, so that the launch's tail is a third of a unit (MB = 3) rather than a whole one.
-    const int r_full = a.n_cand >= V ? 1 + (a.n_cand - V) / n_waves : 0;
-    const int N_full = r_full > 0 ? V + (r_full - 1) * n_waves : 0;
+    // Fewer units than round-0 waves: one round of whole units (a sub-unit costs a wave about as
+    // long as a whole one, so cutting them up would only multiply the reads).
+    const int r_full = a.n_cand >= V ? 1 + (a.n_cand - V) / n_waves : (a.n_cand > 0 ? 1 : 0);
+    const int N_full = r_full > 0 ? imin_t(a.n_cand, V + (r_full - 1) * n_waves) : 0;
     const int n_sub = (a.n_cand - N_full) * MB;
     auto cand_of = [&](int k) {   // k-th full candidate unit of this wave (N_full when none)
         const int c = w >= nuw ? (k == 0 ? wr : V + (k - 1) * n_waves + wr) : V + k * n_waves + wr;

@@ -22,8 +22,8 @@ ROWS_LINES = [
     "const int nuw = both ? imin_t(shared ? (a.n_user + wpb - 1) / wpb * wpb : a.n_user, n_waves) : 0;",
     "const int V = n_waves - nuw;",
     "const int wr = n_waves - 1 - w;",
-    "const int r_full = a.n_cand >= V ? 1 + (a.n_cand - V) / n_waves : 0;",
-    "const int N_full = r_full > 0 ? V + (r_full - 1) * n_waves : 0;",
+    "const int r_full = a.n_cand >= V ? 1 + (a.n_cand - V) / n_waves : (a.n_cand > 0 ? 1 : 0);",
+    "const int N_full = r_full > 0 ? imin_t(a.n_cand, V + (r_full - 1) * n_waves) : 0;",
     "const int n_sub = (a.n_cand - N_full) * MB;",
     "const int c = w >= nuw ? (k == 0 ? wr : V + (k - 1) * n_waves + wr) : V + k * n_waves + wr;",
     "for (int sidx = wr; sidx < n_sub;) {",
@@ -42,8 +42,8 @@ def rows_schedule(n_waves, wpb, n_user, n_cand, MB, lds_shared):
     shared = both and lds_shared
     nuw = min(-(-n_user // wpb) * wpb if shared else n_user, n_waves) if both else 0
     V = n_waves - nuw
-    r_full = 1 + (n_cand - V) // n_waves if n_cand >= V else 0
-    N_full = V + (r_full - 1) * n_waves if r_full > 0 else 0
+    r_full = 1 + (n_cand - V) // n_waves if n_cand >= V else (1 if n_cand > 0 else 0)
+    N_full = min(n_cand, V + (r_full - 1) * n_waves) if r_full > 0 else 0
     n_sub = (n_cand - N_full) * MB
     out = []
     for w in range(n_waves):
@@ -81,6 +81,8 @@ def test_rows_schedule_covers_every_unit_once(case):
     assert fulls == list(range(N_full))
     subs = sorted(s for _, _, ss in sched for s in ss)
     assert subs == list(range((n_cand - N_full) * MB))
+    if n_cand <= V:
+        assert N_full == n_cand                  # a single round: whole units, no sub-units
     if n_user > 0 and n_cand > 0:
         for w, (u, cs, _) in enumerate(sched):
             assert len(u) <= 1 and (not u or u[0] == w)        # a user unit is a wave's first unit
