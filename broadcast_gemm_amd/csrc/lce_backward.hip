@@ -261,50 +261,65 @@ __global__ void __launch_bounds__(256) wgrad_kernel(WgradArgs args) {
 }
 
 // dW_c[m][k] = sum over chunks of part_c; dW_u[m][k] = sum over chunks of the hi row m and
-// the lo row M + m of part_u.  A block takes 32 outputs; its 8 thread groups each add a run
-// of consecutive chunks (their loads all in flight), and the 8 run sums are then added in
-// run order, so the result does not depend on the launch.
+// the lo row M + m of part_u.  A block takes 32 groups of V consecutive outputs (V = 4: one
+// 16-byte load per chunk, when every row length is a multiple of 4); its 8 thread groups each
+// add a run of consecutive chunks (their loads all in flight), and the 8 run sums are then
+// added in run order, so the result does not depend on the launch or on V.
+template <int V>
 __global__ void __launch_bounds__(256) wgrad_reduce_kernel(WgradReduceArgs a) {
-    __shared__ float part[kReduceRuns][32];
+    __shared__ float part[kReduceRuns][32 * V];
     const int o = (int)(threadIdx.x & 31), run = (int)(threadIdx.x >> 5);
     const long long n_c = (long long)a.M * a.K_c, n_u = (long long)a.M * a.K_u;
-    const long long i = (long long)blockIdx.x * 32 + o;
+    const long long i = ((long long)blockIdx.x * 32 + o) * V;   // a group never straddles n_c
     const bool is_c = i < n_c;
     const int P = is_c ? a.P_c : a.P_u;
     const int per = (P + kReduceRuns - 1) / kReduceRuns;
     const int c0 = run * per, c1 = imin_t(c0 + per, P);
-    float s = 0.0f;
+    using vec = float __attribute__((ext_vector_type(V)));
+    float s[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) s[k] = 0.0f;
     if (i < n_c + n_u) {
         constexpr int QB = 16;
         for (int c = c0; c < c1; c += QB) {
-            float v[QB], w[QB];
+            vec v[QB], w[QB];
 #pragma unroll
             for (int q = 0; q < QB; ++q) {
                 const bool ok = c + q < c1;
-                if (is_c) {
-                    v[q] = ok ? a.part_c[(size_t)(c + q) * n_c + i] : 0.0f;
-                    w[q] = 0.0f;
-                } else {
-                    const float *p = a.part_u + (size_t)(c + q) * 2 * n_u + (i - n_c);
-                    v[q] = ok ? p[0] : 0.0f;
-                    w[q] = ok ? p[n_u] : 0.0f;
+                v[q] = w[q] = (vec)0.0f;
+                if (ok) {
+                    if (is_c) {
+                        v[q] = *reinterpret_cast<const vec *>(a.part_c + (size_t)(c + q) * n_c + i);
+                    } else {
+                        const float *p = a.part_u + (size_t)(c + q) * 2 * n_u + (i - n_c);
+                        v[q] = *reinterpret_cast<const vec *>(p);
+                        w[q] = *reinterpret_cast<const vec *>(p + n_u);
+                    }
                 }
             }
 #pragma unroll
-            for (int q = 0; q < QB; ++q) {
-                s += v[q];
-                s += w[q];
-            }
+            for (int q = 0; q < QB; ++q)
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    s[k] += v[q][k];
+                    s[k] += w[q][k];
+                }
         }
     }
-    part[run][o] = s;
+#pragma unroll
+    for (int k = 0; k < V; ++k) part[run][o * V + k] = s[k];
     __syncthreads();
     if (run == 0 && i < n_c + n_u) {
-        float t = part[0][o];
+        vec t;
 #pragma unroll
-        for (int r = 1; r < kReduceRuns; ++r) t += part[r][o];
-        if (is_c) a.dW_c[i] = t;
-        else a.dW_u[i - n_c] = t;
+        for (int k = 0; k < V; ++k) {
+            float x = part[0][o * V + k];
+#pragma unroll
+            for (int r = 1; r < kReduceRuns; ++r) x += part[r][o * V + k];
+            t[k] = x;
+        }
+        if (is_c) *reinterpret_cast<vec *>(a.dW_c + i) = t;
+        else *reinterpret_cast<vec *>(a.dW_u + (i - n_c)) = t;
     }
 }
 
@@ -370,7 +385,10 @@ hipError_t launch_wgrad(const WgradArgs &a, hipStream_t s) {
 hipError_t launch_wgrad_reduce(const WgradReduceArgs &a, hipStream_t s) {
     const long long n = (long long)a.M * (a.K_u + a.K_c);
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + 31) / 32)), dim3(256), 0, s, a);
+    if ((long long)a.M * a.K_c % 4 == 0 && (long long)a.M * a.K_u % 4 == 0)
+        hipLaunchKernelGGL(wgrad_reduce_kernel<4>, dim3((unsigned)((n + 127) / 128)), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(wgrad_reduce_kernel<1>, dim3((unsigned)((n + 31) / 32)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
