@@ -41,6 +41,7 @@ DTYPES = {"bf16": 0, "f32": 1}
 VARIANTS = {"auto": 0, "S0": 1, "S1": 2, "S2": 3, "S3": 4, "S4": 5}
 FLAG_DEBUG_DELAY_USER = 2
 FLAG_DEBUG_SKIP_USER = 4
+FLAG_DEBUG_POISON_USER = 16
 FLAG_BACKWARD = 8
 
 # Every symbol include/ikbo.h declares.

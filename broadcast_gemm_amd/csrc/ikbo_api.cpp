@@ -184,7 +184,8 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
     if (max_B_u < 1 || max_B_c < 0 || K_u < 1 || K_c < 1 || M < 1 || D < 1) return IKBO_ERR_INVALID_ARG;
     if (dtype != IKBO_DTYPE_BF16 && dtype != IKBO_DTYPE_F32) return IKBO_ERR_INVALID_ARG;
     if (variant < IKBO_VARIANT_AUTO || variant > IKBO_S4_PERSISTENT) return IKBO_ERR_INVALID_ARG;
-    if (flags & ~(unsigned)(IKBO_FLAG_DEBUG_DELAY_USER | IKBO_FLAG_DEBUG_SKIP_USER | IKBO_FLAG_BACKWARD))
+    if (flags & ~(unsigned)(IKBO_FLAG_DEBUG_DELAY_USER | IKBO_FLAG_DEBUG_SKIP_USER | IKBO_FLAG_BACKWARD |
+                            IKBO_FLAG_DEBUG_POISON_USER))
         return IKBO_ERR_INVALID_ARG;
     if (variant == IKBO_VARIANT_AUTO) variant = IKBO_S4_PERSISTENT;
     const int elt = dtype == IKBO_DTYPE_BF16 ? 2 : 4;
@@ -804,6 +805,13 @@ int ikbo_lce_forward(ikbo_lce_plan_t p, const void *U, const void *C, const int3
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     if (cur != p->device) return IKBO_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((p->flags & IKBO_FLAG_DEBUG_POISON_USER) && p->P_u != nullptr) {
+        // Every user partial starts this forward as a quiet NaN: a candidate that reads P_u
+        // before this forward's user product has written it carries the NaN into Y.
+        if ((e = hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(p->P_u), 0x7fc00000u, (size_t)B_u * M * D, s)) !=
+            hipSuccess)
+            return hip_fail(e, "poison P_u");
+    }
     if (p->engine == ENGINE_STREAM) return forward_stream(p, U, C, map, W_u, W_c, Y, B_u, B_c, s);
     if (p->engine == ENGINE_ROWS) return forward_rows(p, U, C, map, W_u, W_c, Y, B_u, B_c, s);
     return forward_flat(p, U, C, map, W_u, W_c, Y, B_u, B_c, s);

@@ -79,7 +79,8 @@ enum {
 enum {
     IKBO_FLAG_DEBUG_DELAY_USER = 2, /* S4: user tiles sleep before computing (exercises the wait) */
     IKBO_FLAG_DEBUG_SKIP_USER = 4,  /* S4: user tiles publish nothing; candidates time out */
-    IKBO_FLAG_BACKWARD = 8          /* also allocate the workspace of ikbo_lce_backward */
+    IKBO_FLAG_BACKWARD = 8,         /* also allocate the workspace of ikbo_lce_backward */
+    IKBO_FLAG_DEBUG_POISON_USER = 16 /* each forward first fills the user partials P_u with NaN */
 };
 
 /*

@@ -262,6 +262,44 @@ def test_s4_delayed_user_tiles_still_correct():
     assert_close(to_f64(Y), oracle.lce_f64(x.U, x.C, x.map, x.W_u, x.W_c), "S4 delayed users")
 
 
+@pytest.mark.parametrize("engine", ["rows", "stream"])
+@pytest.mark.parametrize("name", ["default-70to1", "small-10to1"])
+@pytest.mark.parametrize("delay", [False, True])
+def test_s4_poisoned_user_partials(name, engine, delay, monkeypatch):
+    """Each forward first fills the user partials with NaN (and, with delay, the user units
+    also sleep before computing): a candidate that read P_u before this forward's user
+    product had published it would carry a NaN into Y.  Two forwards in a row, every element
+    against the oracle."""
+    log(f"[s4-poison] config={name} engine={engine} delay={delay}")
+    monkeypatch.setenv("IKBO_STREAM", "1" if engine == "stream" else "0")
+    cfg = CONFIG_BY_NAME[name]
+    x = cached_inputs(name)
+    ref, rows = cached_oracle(name)
+    flags = bga.FLAG_DEBUG_POISON_USER | (bga.FLAG_DEBUG_DELAY_USER if delay else 0)
+    with bga.LcePlan(cfg.B_u, cfg.B_c, cfg.K_u, cfg.K_c, cfg.M, cfg.D, variant="S4", flags=flags) as p:
+        assert p.info()["engine"] == engine
+        for k in range(2):
+            Y = run(x, "S4", plan=p)
+            assert p.check() == bga.IKBO_OK
+            Yf = to_f64(Y)
+            assert not np.isnan(Yf).any(), f"forward {k}: NaN from a poisoned user partial"
+            assert_close(Yf if rows is None else Yf[rows], ref, f"S4/{engine} poisoned forward {k}")
+
+
+def test_s4_poison_reaches_the_user_partials():
+    """The poisoning itself: with the user units skipped, every candidate times out and then
+    adds the poisoned partials, so every output is NaN and the plan reports the timeout."""
+    log("[s4-poison-skip]")
+    cfg = CONFIG_BY_NAME["small-10to1"]
+    x = cached_inputs("small-10to1")
+    with bga.LcePlan(cfg.B_u, cfg.B_c, cfg.K_u, cfg.K_c, cfg.M, cfg.D, variant="S4",
+                     flags=bga.FLAG_DEBUG_POISON_USER | bga.FLAG_DEBUG_SKIP_USER) as p:
+        p.set_spin_limit(200)
+        Y = run(x, "S4", plan=p, check=False)
+        assert p.check() == bga.IKBO_ERR_TIMEOUT
+        assert np.isnan(to_f64(Y)).all()
+
+
 def test_s4_skipped_user_tiles_time_out():
     """No user tile publishes: every candidate wave gives up after the poll limit,
     the kernel exits, and the plan reports IKBO_ERR_TIMEOUT."""
