@@ -50,6 +50,8 @@ struct ikbo_lce_plan_s {
     // rows engine
     int rows_mb;
     int rows_lds_shared;            // S4: W_u and W_c share one LDS region (their sum does not fit)
+    int rows_tail_split;            // S3/S4: a partial last round's units are cut along K (lce_rows.hip)
+    int rows_tail_lds;              // LDS bytes of those pieces' partial sums
     int bpc_user, bpc_cand, bpc_both;
     // stream engine
     int st_mb, st_nmc, st_nrb, st_ncb;
@@ -233,6 +235,13 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
         if (variant == IKBO_S0_MATERIALISED) fits = lds_cat <= (size_t)max_lds;
         else fits = std::max(lds_u, lds_c) <= (size_t)max_lds;
         p->rows_lds_shared = variant == IKBO_S4_PERSISTENT && lds_u + lds_c > (size_t)max_lds ? 1 : 0;
+        // Tail pieces: four waves' partial sums of a unit (MB row blocks of 16 x D fp32 each) in LDS;
+        // each of the four pieces needs a K step of its own.
+        p->rows_tail_lds = 4 * mb * 16 * D * 4;
+        p->rows_tail_split = (variant == IKBO_S3_EPILOGUE_FUSED || variant == IKBO_S4_PERSISTENT) &&
+                                     ceil_div(K_c, 32) >= 4 && p->rows_tail_lds <= max_lds &&
+                                     env_int("IKBO_TAIL_SPLIT", 1) != 0
+                                 ? 1 : 0;
         // Epilogue byte offsets within one fp32 [M_pad][D] matrix are 32-bit.
         if (fits && (long long)mpad * D * 4 < (1LL << 31)) {
             p->engine = ENGINE_ROWS;
@@ -441,6 +450,8 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
         auto bpc = [&](int nu, int nc) {
             r.n_user = nu; r.n_cand = nc;
             r.lds_shared = nu > 0 && nc > 0 ? p->rows_lds_shared : 0;
+            r.tail_split = nc > 0 && epi == EPI_ADD_USER ? p->rows_tail_split : 0;
+            r.tail_lds_bytes = p->rows_tail_lds;
             if (rows_lds_bytes(r) > (size_t)max_lds) return 0;
             return rows_blocks_per_cu(epi, D, p->rows_mb, rows_lds_bytes(r));
         };
@@ -506,13 +517,15 @@ int ikbo_lce_plan_info(ikbo_lce_plan_t p, char *json, size_t cap) {
                      "\"vec\":%d,\"K_u_pad\":%d,\"K_c_pad\":%d,\"K_cat_pad\":%d,\"user_ksplit\":%d,"
                      "\"user_ksteps_per_split\":%d,\"blocks_per_cu\":[%d,%d,%d],\"fused_grid\":%d,"
                      "\"n_cu\":%d,\"workspace_bytes\":%zu,\"backward\":%d,\"bwd_dc_mb\":%d,"
-                     "\"bwd_du_mb\":%d,\"bwd_seg_chunks\":%d,\"bwd_wgc_chunks\":%d,\"bwd_wgu_chunks\":%d}",
+                     "\"bwd_du_mb\":%d,\"bwd_seg_chunks\":%d,\"bwd_wgc_chunks\":%d,\"bwd_wgu_chunks\":%d,"
+                     "\"rows_tail_split\":%d}",
                      names[p->variant], p->dtype == IKBO_DTYPE_BF16 ? "bf16" : "f32",
                      p->engine == ENGINE_STREAM ? "stream" : rows ? "rows" : "flat",
                      p->max_B_u, p->max_B_c, p->K_u, p->K_c, p->M, p->D, rows ? p->rows_mb : p->tile.mb,
                      p->n_mchunks, p->M_pad, rows ? 0 : p->tile.vec, p->ldw_u, p->ldw_c, p->ldw_cat, p->ksplit,
                      p->ks_per_split, p->bpc_user, p->bpc_cand, p->bpc_both, p->fused_grid, p->n_cu,
-                     p->arena_bytes, p->bwd, p->dc_mb, p->du_tile.mb, p->seg_T, p->wgc_chunks, p->wgu_chunks);
+                     p->arena_bytes, p->bwd, p->dc_mb, p->du_tile.mb, p->seg_T, p->wgc_chunks, p->wgu_chunks,
+                     rows ? p->rows_tail_split : 0);
     if (n < 0) return IKBO_ERR_INVALID_ARG;
     if (cap > 0) {
         size_t c = std::min((size_t)n, cap - 1);
@@ -569,6 +582,7 @@ int forward_rows(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t 
     a.n_mblocks = p->n_mblocks;
     a.spin_limit = p->spin_limit;
     a.debug_flags = p->flags;
+    a.tail_lds_bytes = p->rows_tail_lds;
     const int n_user = B_u * p->n_mblocks;
     const int n_cand = B_c * p->n_mchunks;
     hipError_t e;
@@ -609,6 +623,7 @@ int forward_rows(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t 
             if ((e = rows_launch(p, EPI_ADD_USER, u, p->bpc_user, s)) != hipSuccess) return hip_fail(e, "user gemm");
             RowArgs c = a;
             c.n_user = 0; c.n_cand = n_cand; c.out = Y; c.wait_flags = 0;   // stream order publishes P_u
+            c.tail_split = p->rows_tail_split;
             if ((e = rows_launch(p, EPI_ADD_USER, c, p->bpc_cand, s)) != hipSuccess) return hip_fail(e, "cand gemm");
             break;
         }
@@ -624,6 +639,7 @@ int forward_rows(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t 
             if (cap == hipStreamCaptureStatusNone && n_user <= waves) {
                 RowArgs f = a;
                 f.n_user = n_user; f.n_cand = n_cand; f.out = Y; f.wait_flags = 1;
+                f.tail_split = p->rows_tail_split;
                 f.lds_shared = p->rows_lds_shared;
                 f.epoch = ++p->epoch;
                 if (f.epoch == 0) f.epoch = ++p->epoch;   // 0 is the flags' initial value
@@ -635,6 +651,7 @@ int forward_rows(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t 
             if ((e = rows_launch(p, EPI_ADD_USER, u, p->bpc_user, s)) != hipSuccess) return hip_fail(e, "user gemm");
             RowArgs c = a;
             c.n_user = 0; c.n_cand = n_cand; c.out = Y; c.wait_flags = 0;
+            c.tail_split = p->rows_tail_split;
             if ((e = rows_launch(p, EPI_ADD_USER, c, p->bpc_cand, s)) != hipSuccess) return hip_fail(e, "cand gemm");
             break;
         }

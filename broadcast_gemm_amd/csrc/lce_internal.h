@@ -130,6 +130,8 @@ struct RowArgs {
     int wait_flags;               // users publish and candidates wait (users in the same launch)
     int lds_shared;               // W_u and W_c take turns in one LDS region (both do not fit at once)
     int xcd_order;                // number blocks XCD by XCD (see lce_rows.hip)
+    int tail_split;               // a partial last round's units are split along K over a block's four waves
+    int tail_lds_bytes;           // LDS those pieces' partial sums take (0 without tail_split)
     uint32_t spin_limit;
     uint32_t debug_flags;
 };

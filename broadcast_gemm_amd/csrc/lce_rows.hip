@@ -272,7 +272,18 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     // long as a whole one, so cutting them up would only multiply the reads).
     const int r_full = a.n_cand >= V ? 1 + (a.n_cand - V) / n_waves : (a.n_cand > 0 ? 1 : 0);
     const int N_full = r_full > 0 ? imin_t(a.n_cand, V + (r_full - 1) * n_waves) : 0;
-    const int n_sub = (a.n_cand - N_full) * MB;
+    // With tail_split (and L at most a quarter of the waves) the L units of a partial last round
+    // are instead cut along K: the four waves of one block (the last L blocks, wr / 4 = unit) each
+    // multiply a share of the unit's K steps
+    // into all its rows, and the block adds the four partial sums in LDS, one row block per wave.
+    // A wave's piece then reads a quarter of C[b] where a sub-unit reads all of it.
+    const int n_left = a.n_cand - N_full;
+    const bool tsplit = EPI == EPI_ADD_USER && a.tail_split && n_left > 0 && 4 * n_left <= n_waves;
+    const int n_sub = tsplit ? 0 : n_left * MB;
+    const bool has_piece = tsplit && wr < 4 * n_left;       // block-uniform: wr / 4 is the block's
+    const int tq = wr & 3;                                  // this wave's piece
+    const int tk_n = a.n_ks_c / 4 + (tq < a.n_ks_c % 4 ? 1 : 0);
+    const int tk0 = tq * (a.n_ks_c / 4) + imin_t(tq, a.n_ks_c % 4);
     auto cand_of = [&](int k) {   // k-th full candidate unit of this wave (N_full when none)
         const int c = w >= nuw ? (k == 0 ? wr : V + (k - 1) * n_waves + wr) : V + k * n_waves + wr;
         return c < N_full ? c : N_full;
@@ -287,9 +298,17 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         return sidx < n_sub ? uniform_rsrc(a.C + (size_t)((N_full + sidx / MB) / n_mc) * a.K_c * D, a.K_c * D * 2)
                             : uniform_rsrc(nullptr, 0);
     };
-    // X of full unit c; past the full units, the X of this wave's first sub-unit.
+    // This wave's rows of C for its tail piece (none without one).
+    auto piece_rsrc = [&]() {
+        const int rows = imin_t(a.K_c - tk0 * 32, tk_n * 32);
+        return has_piece ? uniform_rsrc(a.C + (size_t)((N_full + wr / 4) / n_mc) * a.K_c * D + (size_t)tk0 * 32 * D,
+                                        rows * D * 2)
+                         : uniform_rsrc(nullptr, 0);
+    };
+    // X of full unit c; past the full units, the X of this wave's first sub-unit or tail piece.
     auto cand_rsrc = [&](int c) {
-        return c < N_full ? uniform_rsrc(a.C + (size_t)(c / n_mc) * a.K_c * D, a.K_c * D * 2) : sub_rsrc(wr);
+        return c < N_full ? uniform_rsrc(a.C + (size_t)(c / n_mc) * a.K_c * D, a.K_c * D * 2)
+                          : (tsplit ? piece_rsrc() : sub_rsrc(wr));
     };
 
     // The map through scalar loads (wave-uniform indices): a vector load would be waited for
@@ -420,7 +439,7 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
                 T.zero();
                 T.run(rs1, rs2, a.n_ks_c, wl_c, a.K_wc, a.M, (c1 % n_mc) * MB * 16, g, j);
             }
-            if (u0 >= 0 && u0 < a.B_u && (c2 < N_full || wr < n_sub)) {
+            if (u0 >= 0 && u0 < a.B_u && (c2 < N_full || wr < n_sub || has_piece)) {
                 // A wave with units after the pair checks every flag once, right after its first
                 // wait (a wave without them has nothing to gain from it).
                 wait_user(u0, c % n_mc);
@@ -466,6 +485,52 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         c = cn;
         ++kc;
         rs = rs_next;
+    }
+
+    // ---- tail pieces: a quarter of the K steps of a partial last round's unit ----
+    if constexpr (EPI == EPI_ADD_USER) {
+        if (has_piece) {
+            const int unit = N_full + wr / 4;
+            const int mc = unit % n_mc;
+            const int b = unit / n_mc;
+            const int mrow0 = mc * MB * 16;
+            T.zero();
+            T.run(rs, uniform_rsrc(nullptr, 0), tk_n, wl_c, a.K_wc, a.M, mrow0, g, j, tk0);
+            // The partial sums overwrite the projections once every wave of the block is done
+            // with them: piece q's block mb, column slot t at vector ((q * MB + mb) * NT + t) * 64.
+            __syncthreads();
+            f32x4_t *part = reinterpret_cast<f32x4_t *>(lds);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int t = 0; t < R::NT; ++t)
+                    part[((tq * MB + mb) * R::NT + t) * 64 + lane] =
+                        (f32x4_t){in_vgpr(T.acc[mb][t][0]), in_vgpr(T.acc[mb][t][1]), in_vgpr(T.acc[mb][t][2]),
+                                  in_vgpr(T.acc[mb][t][3])};
+            __syncthreads();
+            // Wave tq stores row block tq: P_u rows + the four pieces in K order.
+            if (tq < MB) {
+                const int u = (int)__builtin_amdgcn_readfirstlane(map_s[b]);
+                if (u >= 0 && u < a.B_u) {
+                    if (!all_ready) wait_user(u, mc, tq, 1);
+                    float v[4][R::NT];
+                    R::template load_block<kSc1>(uniform_rsrc(a.P_u + (size_t)u * a.M * D, a.M * D * 4),
+                                                 R::off1(mrow0, g, j, 4), R::off2(mrow0, g, j, 4), tq, v);
+#pragma unroll 1
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int t = 0; t < R::NT; ++t) {
+                            const f32x4_t x = part[((q * MB + tq) * R::NT + t) * 64 + lane];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) v[r][t] += x[r];
+                        }
+                    R::store_block_bf16(uniform_rsrc(static_cast<uint16_t *>(a.out) + (size_t)b * a.M * D, a.M * D * 2),
+                                        R::off1(mrow0, g, j, 2), R::off2(mrow0, g, j, 2), tq, v);
+                } else if (lane == 0) {
+                    atomicOr(a.err, ERRBIT_MAP);
+                }
+            }
+        }
     }
 
     // ---- candidate sub-units (b, mc, one row block) of the partial last round ----
@@ -556,7 +621,8 @@ int rows_max_mb(int D) {
 size_t rows_lds_bytes(const RowArgs &a) {
     const size_t c = a.n_cand > 0 ? (size_t)lds_w_elems(a.M, a.K_wc) * 2 : 0;
     const size_t u = a.n_user > 0 ? (size_t)lds_w_elems(a.M, a.K_u) * 2 : 0;
-    return a.lds_shared && a.n_user > 0 && a.n_cand > 0 ? std::max(c, u) : c + u;
+    const size_t w = a.lds_shared && a.n_user > 0 && a.n_cand > 0 ? std::max(c, u) : c + u;
+    return std::max(w, a.tail_split ? (size_t)a.tail_lds_bytes : (size_t)0);   // tail pieces reuse the same LDS
 }
 
 int rows_blocks_per_cu(int epi, int D, int mb, size_t lds_bytes) {

@@ -204,14 +204,16 @@ struct RowTile {
     // fall past the padded end go to the first NS-1 steps of the next matrix
     // (rs_next; a zero-sized resource when there is none), so the ring holds the
     // next unit's opening steps while this unit's epilogue runs.
+    // k0: the matrix's K step 0 is step k0 of W (a piece of a longer product).
     template <int S, int MBX>
     __device__ __forceinline__ void step(f32x4_t (&A)[MB][NT], __amdgpu_buffer_rsrc_t rs,
                                          __amdgpu_buffer_rsrc_t rs_next, int ks, int n_ks, int nsp,
-                                         const uint16_t *wl, int K, int M, int mrow0, bool ragged, int g, int j) {
+                                         const uint16_t *wl, int K, int M, int mrow0, bool ragged, int g, int j,
+                                         int k0) {
         const int kk = ks + S + NS - 1;
         const bool cur = kk < nsp;
         load<(S + NS - 1) % NS>(cur ? rs : rs_next, cur ? kk : kk - nsp);
-        if (ks + S < n_ks) compute<S, MBX>(A, wl, K, M, mrow0, ks + S, ks + S == n_ks - 1, ragged, g, j);
+        if (ks + S < n_ks) compute<S, MBX>(A, wl, K, M, mrow0, k0 + ks + S, ks + S == n_ks - 1, ragged, g, j);
     }
 
     // MBX <= MB row blocks from mrow0, accumulated into blocks 0 .. MBX-1 of A (a tile's
@@ -219,22 +221,22 @@ struct RowTile {
     template <int MBX = MB>
     __device__ __forceinline__ void run_into(f32x4_t (&A)[MB][NT], __amdgpu_buffer_rsrc_t rs,
                                              __amdgpu_buffer_rsrc_t rs_next, int n_ks, const uint16_t *wl, int K,
-                                             int M, int mrow0, int g, int j) {
+                                             int M, int mrow0, int g, int j, int k0 = 0) {
         static_assert(MBX >= 1 && MBX <= MB, "row blocks");
         const int nsp = (n_ks + NS - 1) / NS * NS;
         const bool ragged = mrow0 + 16 * MBX > M;
         for (int ks = 0; ks < nsp; ks += NS) {
-            step<0, MBX>(A, rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
-            if constexpr (NS > 1) step<1, MBX>(A, rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
-            if constexpr (NS > 2) step<2, MBX>(A, rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
-            if constexpr (NS > 3) step<3, MBX>(A, rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j);
+            step<0, MBX>(A, rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j, k0);
+            if constexpr (NS > 1) step<1, MBX>(A, rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j, k0);
+            if constexpr (NS > 2) step<2, MBX>(A, rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j, k0);
+            if constexpr (NS > 3) step<3, MBX>(A, rs, rs_next, ks, n_ks, nsp, wl, K, M, mrow0, ragged, g, j, k0);
         }
     }
 
     template <int MBX = MB>
     __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rs_next, int n_ks,
-                                        const uint16_t *wl, int K, int M, int mrow0, int g, int j) {
-        run_into<MBX>(acc, rs, rs_next, n_ks, wl, K, M, mrow0, g, j);
+                                        const uint16_t *wl, int K, int M, int mrow0, int g, int j, int k0 = 0) {
+        run_into<MBX>(acc, rs, rs_next, n_ks, wl, K, M, mrow0, g, j, k0);
     }
 
     // Column of output t for lane slot j.

@@ -69,3 +69,42 @@ def test_schedule_shapes(shape, variant, engine, monkeypatch):
     finally:
         plan.close()
     assert_close(Y, oracle.lce_f64(x.U, x.C, x.map, x.W_u, x.W_c), f"{shape}/{variant}")
+
+
+TAIL_SHAPES = [
+    # (B_u, B_c, K_u, K_c, M, D, map): units left for a partial last round, at most a quarter of the
+    # waves, so that each is cut along K over the four waves of one block
+    (9, 1100, 120, 130, 64, 32, "sorted"),       # D = 32, 112 units left (S3's candidate launch: 76)
+    (9, 1100, 120, 130, 64, 64, "random"),       # D = 64
+    (9, 600, 120, 130, 128, 128, "sorted"),      # D = 128, four row blocks per unit (128 KB of partials)
+    (9, 1100, 120, 130, 48, 192, "random"),      # D = 192, one row block per unit
+    (15, 1000, 301, 197, 90, 160, "sorted"),     # 42 units left, ragged last row chunk
+    (7, 1150, 509, 251, 128, 128, "random"),     # projections taking turns in LDS (S4); S3 leaves 252 units
+]
+
+
+@pytest.mark.parametrize("variant", ["S3", "S4"])
+@pytest.mark.parametrize("shape", TAIL_SHAPES,
+                         ids=[f"{s[0]}x{s[1]}-K{s[2]}_{s[3]}-M{s[4]}-D{s[5]}-{s[6]}" for s in TAIL_SHAPES])
+def test_tail_pieces(shape, variant, monkeypatch):
+    """The partial last round's units cut along K into four pieces on the waves of one block,
+    their partial sums added in LDS (the gather-add stages on the rows engine), against the
+    oracle; a second forward on the same plan as well."""
+    import oracle
+    B_u, B_c, K_u, K_c, M, D, mp = shape
+    log(f"[tail] shape={shape} variant={variant}")
+    cfg = LceConfig("tail", B_u, B_c, K_u, K_c, M, D, "bf16", mp, 97)
+    x = make_inputs(cfg)
+    monkeypatch.setenv("IKBO_STREAM", "0")
+    plan = bga.LcePlan(B_u, B_c, K_u, K_c, M, D, dtype="bf16", variant=variant)
+    try:
+        info = plan.info()
+        assert info["engine"] == "rows" and info["rows_tail_split"] == 1
+        for _ in range(2):
+            Y = plan.forward(*dev_inputs(x))
+            st = plan.check()
+            assert st == bga.IKBO_OK, bga.status_str(st)
+        Y = to_f64(Y)
+    finally:
+        plan.close()
+    assert_close(Y, oracle.lce_f64(x.U, x.C, x.map, x.W_u, x.W_c), f"{shape}/{variant} tail pieces")

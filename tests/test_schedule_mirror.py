@@ -24,7 +24,18 @@ ROWS_LINES = [
     "const int wr = n_waves - 1 - w;",
     "const int r_full = a.n_cand >= V ? 1 + (a.n_cand - V) / n_waves : (a.n_cand > 0 ? 1 : 0);",
     "const int N_full = r_full > 0 ? imin_t(a.n_cand, V + (r_full - 1) * n_waves) : 0;",
-    "const int n_sub = (a.n_cand - N_full) * MB;",
+    "const int n_left = a.n_cand - N_full;",
+    "const bool tsplit = EPI == EPI_ADD_USER && a.tail_split && n_left > 0 && 4 * n_left <= n_waves;",
+    "const int n_sub = tsplit ? 0 : n_left * MB;",
+    "const bool has_piece = tsplit && wr < 4 * n_left;",
+    "const int tq = wr & 3;",
+    "const int tk_n = a.n_ks_c / 4 + (tq < a.n_ks_c % 4 ? 1 : 0);",
+    "const int tk0 = tq * (a.n_ks_c / 4) + imin_t(tq, a.n_ks_c % 4);",
+    "const int rows = imin_t(a.K_c - tk0 * 32, tk_n * 32);",
+    "return has_piece ? uniform_rsrc(a.C + (size_t)((N_full + wr / 4) / n_mc) * a.K_c * D + (size_t)tk0 * 32 * D,",
+    "const int unit = N_full + wr / 4;",
+    "part[((tq * MB + mb) * R::NT + t) * 64 + lane] =",
+    "const f32x4_t x = part[((q * MB + tq) * R::NT + t) * 64 + lane];",
     "const int c = w >= nuw ? (k == 0 ? wr : V + (k - 1) * n_waves + wr) : V + k * n_waves + wr;",
     "for (int sidx = wr; sidx < n_sub;) {",
 ]
@@ -88,6 +99,69 @@ def test_rows_schedule_covers_every_unit_once(case):
             assert len(u) <= 1 and (not u or u[0] == w)        # a user unit is a wave's first unit
             if cs and cs[0] < V:
                 assert w >= nuw                                  # round 0 skips the user waves
+
+
+def tail_pieces(n_waves, n_cand, N_full, n_ks_c):
+    """wave -> (unit, first K step, K steps) of its tail piece, as the kernel assigns them."""
+    n_left = n_cand - N_full
+    out = {}
+    if not 0 < 4 * n_left <= n_waves:                # otherwise sub-units, as without tail_split
+        return out
+    for w in range(n_waves):
+        wr = n_waves - 1 - w
+        if wr < 4 * n_left:
+            tq = wr & 3
+            out[w] = (N_full + wr // 4, tq * (n_ks_c // 4) + min(tq, n_ks_c % 4),
+                      n_ks_c // 4 + (1 if tq < n_ks_c % 4 else 0))
+    return out
+
+
+@pytest.mark.parametrize("n_blocks,n_user,n_cand,K_c", [
+    (256, 90, 2048, 197), (256, 16, 60000, 251), (256, 354, 8192, 197), (167, 156, 512, 197),
+    (256, 90, 2000, 128), (10, 3, 50, 129), (256, 6, 1100, 97), (4, 9, 7, 200)])
+def test_rows_tail_pieces_cover_each_leftover_unit_once(n_blocks, n_user, n_cand, K_c):
+    """With tail_split, each unit of the partial last round is held by the four waves of one
+    block (the block's waves share wr // 4), whose pieces take every K step once; the pieces'
+    C rows stay inside C[b]; and the four partial tiles fit the LDS the host reserves."""
+    n_waves = 4 * n_blocks
+    sched, N_full, nuw, V = rows_schedule(n_waves, 4, n_user, n_cand, 3, False)
+    n_ks_c = -(-K_c // 32)
+    assert n_ks_c >= 4                            # the host splits only then
+    pieces = tail_pieces(n_waves, n_cand, N_full, n_ks_c)
+    if 4 * (n_cand - N_full) > n_waves:
+        assert not pieces                         # more than a quarter round left: sub-units instead
+        return
+    units = {}
+    for w, (unit, k0, nk) in pieces.items():
+        assert nk >= 1
+        rows = min(K_c - k0 * 32, nk * 32)
+        assert rows > 0 and k0 * 32 + rows <= K_c
+        units.setdefault(unit, []).append((w, k0, nk))
+    assert sorted(units) == list(range(N_full, n_cand))
+    for unit, ps in units.items():
+        assert len(ps) == 4 and len({w // 4 for w, _, _ in ps}) == 1
+        steps = sorted(k for _, k0, nk in ps for k in range(k0, k0 + nk))
+        assert steps == list(range(n_ks_c))
+    # no wave holds both a user unit and a tail piece, so a piece never waits behind a user unit
+    for w in pieces:
+        assert not sched[w][0]
+
+
+@pytest.mark.parametrize("MB,D", [(3, 160), (4, 128), (2, 192), (4, 64), (4, 32), (3, 128)])
+def test_rows_tail_partials_fit_their_lds(MB, D):
+    """Piece q's row block mb, column slot t of lane l sits at vector ((q * MB + mb) * NT + t) * 64 + l
+    of 16 bytes: all four pieces' tiles inside 4 * MB * 16 * D * 4 bytes (the host's
+    rows_tail_lds), at most 160 KB, each vector written once."""
+    NT = D // 16
+    seen = set()
+    for q in range(4):
+        for mb in range(MB):
+            for t in range(NT):
+                for lane in range(64):
+                    v = ((q * MB + mb) * NT + t) * 64 + lane
+                    assert v not in seen
+                    seen.add(v)
+    assert max(seen) * 16 + 16 == 4 * MB * 16 * D * 4 <= 160 * 1024
 
 
 # ---- streaming engine (lce_stream.hip) ----
