@@ -583,6 +583,12 @@ int forward_rows(ikbo_lce_plan_t p, const void *U, const void *C, const int32_t 
     a.spin_limit = p->spin_limit;
     a.debug_flags = p->flags;
     a.tail_lds_bytes = p->rows_tail_lds;
+    // Keeping a block's waves in step pays when their epilogues take about the same time, which
+    // holds when every user's P_u stays in L2 (10000:1, 2 users: 372-377 against 395-397 us); with
+    // 59 users' P_u (3.6 MB) per L2, the barriers wait on the slowest epilogue (4096 random: 94-98
+    // against 93 us).
+    const int sync_env = env_int("IKBO_PARTNER_SYNC", -1);
+    a.partner_sync = sync_env >= 0 ? sync_env != 0 : (long long)B_u * M * D * 4 <= (1LL << 20);
     const int n_user = B_u * p->n_mblocks;
     const int n_cand = B_c * p->n_mchunks;
     hipError_t e;

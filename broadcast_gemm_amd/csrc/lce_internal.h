@@ -132,6 +132,7 @@ struct RowArgs {
     int xcd_order;                // number blocks XCD by XCD (see lce_rows.hip)
     int tail_split;               // a partial last round's units are split along K over a block's four waves
     int tail_lds_bytes;           // LDS those pieces' partial sums take (0 without tail_split)
+    int partner_sync;             // blocks without user units pass a barrier before each later full unit
     uint32_t spin_limit;
     uint32_t debug_flags;
 };

@@ -453,6 +453,12 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         }
     }
     while (c < N_full) {
+        // The units of one entry sit on neighbouring waves of a block and stream the same rows of
+        // C: a barrier per unit keeps them in step, so one wave's reads meet the other's in L2
+        // instead of missing after the waves have drifted apart.  When the rounds are complete
+        // (round 0 filled), every wave of a block without user units holds the same number of these
+        // units, so each passes the same barriers.
+        if (a.partner_sync && !need_u && a.n_cand >= V) __syncthreads();
         c = (int)__builtin_amdgcn_readfirstlane(c);
         const int cn = cand_of(kc + 1);
         const __amdgpu_buffer_rsrc_t rs_next = cand_rsrc(cn);

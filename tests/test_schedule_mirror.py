@@ -38,6 +38,7 @@ ROWS_LINES = [
     "const f32x4_t x = part[((q * MB + tq) * R::NT + t) * 64 + lane];",
     "const int c = w >= nuw ? (k == 0 ? wr : V + (k - 1) * n_waves + wr) : V + k * n_waves + wr;",
     "for (int sidx = wr; sidx < n_sub;) {",
+    "if (a.partner_sync && !need_u && a.n_cand >= V) __syncthreads();",
 ]
 
 
@@ -99,6 +100,26 @@ def test_rows_schedule_covers_every_unit_once(case):
             assert len(u) <= 1 and (not u or u[0] == w)        # a user unit is a wave's first unit
             if cs and cs[0] < V:
                 assert w >= nuw                                  # round 0 skips the user waves
+
+
+@pytest.mark.parametrize("case", ROWS_CASES[::5])
+def test_rows_partner_barriers_match_within_a_block(case):
+    """The barrier before each full unit after the first two (one-launch stage) or each full unit
+    (candidate-only launches) is passed only by blocks without user units and only when round 0
+    is complete; every wave of such a block then holds the same number of full units, so the
+    block's waves pass the same barriers (with a single partial round they would not)."""
+    n_waves, wpb, n_user, n_cand, MB, shared = case
+    if wpb != 4:
+        return
+    sched, N_full, nuw, V = rows_schedule(n_waves, wpb, n_user, n_cand, MB, shared)
+    if n_cand < V:                                # a single partial round: no barriers
+        return
+    for b in range(n_waves // wpb):
+        waves = range(b * wpb, (b + 1) * wpb)
+        if b * wpb < n_user:                      # need_u: the block holds user units
+            continue
+        counts = {len(sched[w][1]) for w in waves}
+        assert len(counts) == 1, (b, counts)
 
 
 def tail_pieces(n_waves, n_cand, N_full, n_ks_c):
