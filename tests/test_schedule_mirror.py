@@ -341,3 +341,61 @@ def test_stream_user_tile_reads_stay_in_the_region(K_u):
             assert pa + 64 * s + 16 <= region
     # the DMA of the slice (n_ks_u chunks) and of the W_u rows (ceil(32 K_u / 1024) chunks)
     assert slice_bytes + -(-32 * K_u // 1024) * 1024 <= region
+
+
+
+# ---- row tile (lce_rowtile.h): lane offsets of the activation loads ----
+
+ROWTILE_LINES = [
+    "off1 = (8 * g * DCOV + 8 * j) * 2;",
+    "off2 = (8 * g * DCOV + 128 * N8 + W2 * j) * 2;",
+    "u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off1 + r * DCOV * 2, so, 0));",
+    "if constexpr (W2 == 2) r2[S][r].v = __builtin_amdgcn_raw_buffer_load_b32(rs, off2 + r * DCOV * 2, so, 0);",
+    "u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off2 + r * DCOV * 2, so, 0));",
+    "static __device__ __forceinline__ int col1(int j) { return 8 * j; }",
+    "static __device__ __forceinline__ int col2(int j) { return 128 * N8 + W2 * j; }",
+]
+
+ROW_LAYOUTS = {32: (0, 2), 64: (0, 4), 128: (1, 0), 160: (1, 2), 192: (1, 4)}
+
+
+def test_rowtile_mirror_matches_kernel_source():
+    src = _src("lce_rowtile.h")
+    for line in ROWTILE_LINES:
+        assert " ".join(line.split()) in src, line
+
+
+@pytest.mark.parametrize("D", sorted(ROW_LAYOUTS))
+def test_rowtile_step_loads_cover_the_step_once(D):
+    """The 64 lanes' loads of one K step (16 bytes per row for the 128-column group, W2 * 2
+    bytes per row for the rest) tile its 32 rows x D columns exactly once, each load aligned
+    to its width and inside one row."""
+    N8, W2 = ROW_LAYOUTS[D]
+    DCOV = 128 * N8 + 16 * W2
+    assert DCOV == D
+    seen = [0] * (32 * D * 2)
+    for lane in range(64):
+        g, j = lane >> 4, lane & 15
+        off1 = (8 * g * DCOV + 8 * j) * 2
+        off2 = (8 * g * DCOV + 128 * N8 + W2 * j) * 2
+        loads = [(off1 + r * DCOV * 2, 16) for r in range(8)] if N8 else []
+        loads += [(off2 + r * DCOV * 2, 2 * W2) for r in range(8)] if W2 else []
+        for o, n in loads:
+            assert o % n == 0 and 0 <= o and o + n <= 32 * D * 2
+            assert o // (D * 2) == (o + n - 1) // (D * 2)
+            for b in range(o, o + n):
+                seen[b] += 1
+    assert all(c == 1 for c in seen)
+
+
+@pytest.mark.parametrize("D", sorted(ROW_LAYOUTS))
+def test_rowtile_output_columns_once(D):
+    """Lane slot j's outputs: columns col1(j) + t (t < 8) and col2(j) + t (t < W2); over the 16
+    slots every column once."""
+    N8, W2 = ROW_LAYOUTS[D]
+    cols = []
+    for j in range(16):
+        if N8:
+            cols += [8 * j + t for t in range(8)]
+        cols += [128 * N8 + W2 * j + t for t in range(W2)]
+    assert sorted(cols) == list(range(D))
