@@ -68,6 +68,7 @@ struct ikbo_lce_plan_s {
     int du_nmc, du_ldw;
     int seg_T, seg_slices;                // segment sums: most chunks, 512-element slices
     int wgc_chunks, wgu_chunks;           // most entry chunks of the dW_c and dW_u products
+    int cand_chunks;                      // one-pass dC + dW_c: most chunks (0: separate launches)
     uint16_t *Wt_c, *W_dup, *S2;
     int32_t *perm, *su, *off;
     float *seg_part, *part_c, *part_u;
@@ -353,6 +354,12 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
         p->seg_T = std::max(1, seg_waves / slices);
         p->wgc_chunks = std::max(1, std::min(env_int("IKBO_BWD_WGC_CHUNKS", 128), std::max(max_B_c, 1)));
         p->wgu_chunks = std::max(1, std::min(env_int("IKBO_BWD_WGU_CHUNKS", 64), max_B_u));
+        // dC and the dW_c partials in one pass over the candidates (one chunk per CU), where its
+        // shapes allow.
+        p->cand_chunks = bwd_cand_supported(M, K_c, D) && bwd_cand_lds_bytes(M, D) <= (size_t)max_lds &&
+                                 env_int("IKBO_BWD_FUSED", 1) != 0
+                             ? std::max(1, std::min(p->n_cu, std::max(max_B_c, 1)))
+                             : 0;
         if (p->dc_bpc < 1 || (long long)p->dc_mpad * D * 4 >= (1LL << 31) ||
             bwd_prep_lds_bytes(max_B_u, max_B_c) > (size_t)std::min(max_lds, 64 * 1024)) {
             delete p;
@@ -401,7 +408,7 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
         o_off = take((size_t)(max_B_u + 1) * 4);
         o_seg = take((size_t)(p->seg_T + max_B_u) * MD * 4);
         o_s2 = take((size_t)max_B_u * 2 * MD * 2);
-        o_bpc = take((size_t)p->wgc_chunks * M * K_c * 4);
+        o_bpc = take((size_t)std::max(p->wgc_chunks, p->cand_chunks) * M * K_c * 4);
         o_pu2 = take((size_t)p->wgu_chunks * 2 * M * K_u * 4);
     }
     p->arena_bytes = off;
@@ -518,14 +525,14 @@ int ikbo_lce_plan_info(ikbo_lce_plan_t p, char *json, size_t cap) {
                      "\"user_ksteps_per_split\":%d,\"blocks_per_cu\":[%d,%d,%d],\"fused_grid\":%d,"
                      "\"n_cu\":%d,\"workspace_bytes\":%zu,\"backward\":%d,\"bwd_dc_mb\":%d,"
                      "\"bwd_du_mb\":%d,\"bwd_seg_chunks\":%d,\"bwd_wgc_chunks\":%d,\"bwd_wgu_chunks\":%d,"
-                     "\"rows_tail_split\":%d}",
+                     "\"rows_tail_split\":%d,\"bwd_cand_chunks\":%d}",
                      names[p->variant], p->dtype == IKBO_DTYPE_BF16 ? "bf16" : "f32",
                      p->engine == ENGINE_STREAM ? "stream" : rows ? "rows" : "flat",
                      p->max_B_u, p->max_B_c, p->K_u, p->K_c, p->M, p->D, rows ? p->rows_mb : p->tile.mb,
                      p->n_mchunks, p->M_pad, rows ? 0 : p->tile.vec, p->ldw_u, p->ldw_c, p->ldw_cat, p->ksplit,
                      p->ks_per_split, p->bpc_user, p->bpc_cand, p->bpc_both, p->fused_grid, p->n_cu,
                      p->arena_bytes, p->bwd, p->dc_mb, p->du_tile.mb, p->seg_T, p->wgc_chunks, p->wgu_chunks,
-                     rows ? p->rows_tail_split : 0);
+                     rows ? p->rows_tail_split : 0, p->bwd ? p->cand_chunks : 0);
     if (n < 0) return IKBO_ERR_INVALID_ARG;
     if (cap > 0) {
         size_t c = std::min((size_t)n, cap - 1);
@@ -872,7 +879,16 @@ int ikbo_lce_backward(ikbo_lce_plan_t p, const void *dY, const void *U, const vo
     // side stream 1 beside the caller's stream, which waits for both before the call returns,
     // so that work enqueued after it sees every output.  None of the chains waits on another
     // inside a kernel, so running them side by side cannot stall.
-    const bool fork = env_int("IKBO_BWD_STREAMS", 1) != 0;
+    // The one-pass launch (dC and the dW_c partials) holds every CU, so the other launches gain
+    // nothing from running beside it and it runs on the caller's stream; the cross-stream events
+    // would only add their own latency.
+    // It is taken when each CU's chunk is short (at most 8 candidates: the separate launches'
+    // fixed costs dominate there) or when the K_c row blocks deal out evenly over the four waves
+    // (otherwise the wave with one block more sets the pace of every candidate): measured, at
+    // 4096 candidates and K_c = 197 the separate launches were faster (233 against 259 us).
+    const bool one_pass = p->cand_chunks > 0 && B_c > 0 &&
+                          (ceil_div(B_c, p->n_cu) <= 8 || ceil_div(K_c, 16) % 4 == 0);
+    const bool fork = env_int("IKBO_BWD_STREAMS", one_pass ? 0 : 1) != 0;
     hipStream_t s_dc = s, s_du = s;
     int joined = 0;
     auto join = [&]() -> hipError_t {
@@ -895,8 +911,18 @@ int ikbo_lce_backward(ikbo_lce_plan_t p, const void *dY, const void *U, const vo
         joined = 1;
     }
 
-    // dC[b] = W_c^T . dY[b] on the row-tile engine (W_c^T staged in LDS).
-    if (B_c > 0) {
+    // dC[b] = W_c^T . dY[b], with the dW_c partials in the same pass over the candidates where
+    // the plan allows (one chunk of candidates per CU, from the call's B_c only, so that the
+    // summation order does not depend on the plan's capacity).
+    BwdCandArgs ca{};
+    if (one_pass) {
+        ca.dY = static_cast<const uint16_t *>(dY); ca.C = static_cast<const uint16_t *>(C);
+        ca.W_c = static_cast<const uint16_t *>(W_c); ca.dC = static_cast<uint16_t *>(dC); ca.part = p->part_c;
+        ca.B_c = B_c; ca.M = M; ca.K_c = K_c; ca.D = D;
+        ca.per_chunk = ceil_div(B_c, std::min(std::min(p->n_cu, B_c), std::max(1, env_int("IKBO_BWD_CAND_CHUNKS", p->n_cu))));
+        ca.n_chunks = ceil_div(B_c, ca.per_chunk);
+        if ((e = launch_bwd_cand(ca, s_dc)) != hipSuccess) return fail(e, "bwd dC+dW_c");
+    } else if (B_c > 0) {
         RowArgs c{};
         c.C = static_cast<const uint16_t *>(dY);
         c.W_c = p->Wt_c;
@@ -943,20 +969,31 @@ int ikbo_lce_backward(ikbo_lce_plan_t p, const void *dY, const void *U, const vo
 
     // Weight-gradient partials in one launch: sum over candidates of dY[b] . C[b]^T, and
     // over users of [S_hi; S_lo] . U[u]^T.
+    // (The dW_c partials come from the one-pass launch when it ran.)
     WgradArgs wa{};
-    WgradProblem &wc = wa.p[0], &wu = wa.p[1];
+    WgradProblem wc{}, wu{};
     wc.A = static_cast<const uint16_t *>(dY); wc.B = static_cast<const uint16_t *>(C); wc.part = p->part_c;
     wc.E = B_c; wc.R = M; wc.N = K_c;
     wgrad_problem_setup(wc, p->wgc_chunks);
     wu.A = p->S2; wu.B = static_cast<const uint16_t *>(U); wu.part = p->part_u;
     wu.E = B_u; wu.R = 2 * M; wu.N = K_u;
     wgrad_problem_setup(wu, p->wgu_chunks);
-    wa.n_prob = 2; wa.D = D;
+    if (one_pass) {
+        wa.p[0] = wu;
+        wa.n_prob = 1;
+    } else {
+        wa.p[0] = wc;
+        wa.p[1] = wu;
+        wa.n_prob = 2;
+    }
+    wa.D = D;
     if ((e = launch_wgrad(wa, s)) != hipSuccess) return fail(e, "bwd dW");
 
+    // The reduce reads the one-pass launch's partials: join its stream first.
+    if (one_pass && (e = join()) != hipSuccess) return hip_fail(e, "bwd join");
     WgradReduceArgs ra{};
     ra.part_c = p->part_c; ra.part_u = p->part_u; ra.dW_c = dW_c; ra.dW_u = dW_u;
-    ra.P_c = wc.n_chunks; ra.P_u = wu.n_chunks; ra.M = M; ra.K_u = K_u; ra.K_c = K_c;
+    ra.P_c = one_pass ? ca.n_chunks : wc.n_chunks; ra.P_u = wu.n_chunks; ra.M = M; ra.K_u = K_u; ra.K_c = K_c;
     if ((e = launch_wgrad_reduce(ra, s)) != hipSuccess) return fail(e, "bwd reduce");
     if ((e = join()) != hipSuccess) return hip_fail(e, "bwd join");
     return IKBO_OK;

@@ -32,13 +32,17 @@
 // W_c^T staged in LDS, and the flat engine with [W_u^T | W_u^T] against [S_hi; S_lo].
 #include "ikbo_group.h"
 #include "lce_internal.h"
-#include "lce_rowtile.h"
+#include "lce_stream.h"
+#include "lce_sync.h"
 
 namespace ikbo {
 
 namespace {
 
 constexpr int kReduceRuns = 8;   // thread groups per output in the weight-gradient reduce
+// dC stores are plain write-back: the two halves of a lane's 16-byte run are stored apart in
+// time, and L2 merges them into whole lines.
+constexpr int kDcStore = 0;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -323,6 +327,290 @@ __global__ void __launch_bounds__(256) wgrad_reduce_kernel(WgradReduceArgs a) {
     }
 }
 
+// ---- dC and the dW_c partials in one pass ---------------------------------------------------
+
+// LDS chunk swizzle of the dY copy: 16-byte chunk p of row r holds chunk p ^ cand_sw(r) of the
+// row.  At D = 160 (rows of 80 dwords) rows 4 apart share banks, at D = 128 (64 dwords) every
+// row does; the XOR keeps a chunk inside its group of 4 (D = 160: the last 32 columns stay in
+// chunks 16..19) or of 16.
+template <int D>
+__device__ __forceinline__ int cand_sw(int r) {
+    return D == 128 ? (r & 15) : ((r >> 2) & 3);
+}
+
+// Eight 4-byte LDS reads, waited for in the same statement (the compiler would guard a read it
+// can see with a wait for the direct-to-LDS copies in flight, and with them the HBM reads).
+__device__ __forceinline__ void lds_read_b32x8(uint32_t (&v)[8], const uint32_t (&p)[8]) {
+    asm volatile(
+        "ds_read_b32 %0, %8\n\t"
+        "ds_read_b32 %1, %9\n\t"
+        "ds_read_b32 %2, %10\n\t"
+        "ds_read_b32 %3, %11\n\t"
+        "ds_read_b32 %4, %12\n\t"
+        "ds_read_b32 %5, %13\n\t"
+        "ds_read_b32 %6, %14\n\t"
+        "ds_read_b32 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]));
+}
+
+// Eight 8-byte LDS reads, waited for in the same statement.
+__device__ __forceinline__ void lds_read_b64x8(u32x2_t (&v)[8], const uint32_t (&p)[8]) {
+    asm volatile(
+        "ds_read_b64 %0, %8\n\t"
+        "ds_read_b64 %1, %9\n\t"
+        "ds_read_b64 %2, %10\n\t"
+        "ds_read_b64 %3, %11\n\t"
+        "ds_read_b64 %4, %12\n\t"
+        "ds_read_b64 %5, %13\n\t"
+        "ds_read_b64 %6, %14\n\t"
+        "ds_read_b64 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]));
+}
+
+// One block of four waves per chunk of consecutive candidates (IKBO recsys blog, "Deep Dive:
+// Linear Compression": the candidate side of the product, differentiated).  For each candidate
+// b the block copies dY[b] ([M][D] bf16) into LDS once, by direct-to-LDS loads, double-buffered
+// (the next candidate's copy is in flight while this one is used).  Wave w owns up to four
+// 16-row blocks of K_c (the ceil(K_c/16) blocks dealt out over the four waves) in both products:
+//   dW_c: acc[m][k] += sum_d dY[b][m][d] C[b][k][d]  (A: dY rows from LDS; B: the wave's C rows
+//         from memory, one 16-byte load per fragment; the accumulators stay in registers for the
+//         whole chunk and are written once, as the chunk's partial);
+//   dC:   dC[b][k][d] = sum_m W_c[m][k] dY[b][m][d]  (A: the wave's rows of W_c^T, gathered into
+//         registers once; B: dY from LDS in the row tile's column layout, lane slot j taking 8
+//         rows of columns 8j..8j+7, and of 128+2j, 128+2j+1 at D = 160, transposed in registers,
+//         so that a lane's outputs are runs of consecutive columns of dC).
+// Rows of the copy from M up to the next multiple of 32 read as zero (its source range ends at
+// M rows), and so do W_c^T elements past M or K_c.  Every memory operation of an iteration is
+// issued unconditionally (absent rows and candidates go through empty or out-of-range buffer
+// offsets), so the counts behind each wait are fixed: the wait for the next copy lets exactly
+// the dC stores, the last memory operations before it, stay in flight.
+template <int MR, int W2>
+__global__ void __launch_bounds__(256) bwd_cand_kernel(BwdCandArgs a) {
+    constexpr int D = 128 + 16 * W2;
+    constexpr int KS = D / 32;                    // 32-column steps of the dW_c product
+    constexpr int CH = D / 8;                     // 16-byte chunks per row
+    constexpr int RB = 2 * D;                     // bytes per row
+    constexpr int MSX = (MR + 1) / 2;             // 32-row steps of the dC product (most)
+    constexpr int NI = MSX * RB / 32;             // 1 KB copy instructions for 32*MSX rows
+    constexpr int NQ = (NI + 3) / 4;              // per wave
+    constexpr int BUF = 4 * NQ * 1024;            // bytes per copy buffer
+    constexpr int NST = 32 + (W2 ? 16 : 0);       // dC stores per wave and candidate (< 63)
+    // The next candidate's C loads go out before the dC phase (their latency then hides behind
+    // it) where the registers allow them to stay live across it: all but M > 96 at D = 160.
+    constexpr bool EARLY_C = !(MR == 8 && W2 == 2);
+    extern __shared__ __align__(16) char lds[];
+
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int g = lane >> 4, j = lane & 15;
+    const int e0 = (int)blockIdx.x * a.per_chunk;
+    const int e1 = imin_t(e0 + a.per_chunk, a.B_c);
+    const int nmr = (a.M + 15) / 16, ms = (a.M + 31) / 32;
+    const int n_kb = (a.K_c + 15) / 16;
+    const int nkb = n_kb / 4 + (wv < n_kb % 4 ? 1 : 0);
+    const int k0 = 16 * (wv * (n_kb / 4) + imin_t(wv, n_kb % 4));
+    const int cbytes = a.K_c * RB;                // one C[b] or dC[b] matrix
+    constexpr int kOut = 1 << 30;                 // an offset past every range: reads 0, writes dropped
+
+    // dY[e] into buffer buf: position P = 64 q + lane of the copy (row P / CH, chunk P % CH)
+    // takes the row's chunk (P % CH) ^ cand_sw(row).
+    auto stage = [&](int e, int buf) {
+        const bool ok = e < e1;
+        const __amdgpu_buffer_rsrc_t rs =
+            uniform_rsrc(ok ? a.dY + (size_t)e * a.M * D : nullptr, ok ? a.M * RB : 0);
+        char *dst = lds + buf * BUF;
+        asm volatile("" ::: "memory");   // the counted waits below rely on this issue order
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int q = wv + 4 * i;
+            const int P = 64 * q + lane;
+            const int r = P / CH, c = (P % CH) ^ cand_sw<D>(r);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + 1024 * q), 16,
+                                                     q < NI ? r * RB + 16 * c : kOut, 0, 0, 0);
+        }
+        asm volatile("" ::: "memory");
+    };
+
+    // W_c^T fragments: row k = k0 + 16 nc + j, elements m = 32 s + 8 g .. +7, gathered with
+    // branch-free 2-byte buffer loads (all in flight together): rows m past M lie past the
+    // range, and columns k past the wave's blocks or past K_c go to an out-of-range offset.
+    u32x4_t wt[4][MSX];
+    {
+        const __amdgpu_buffer_rsrc_t rw = uniform_rsrc(a.W_c, a.M * a.K_c * 2);
+#pragma unroll
+        for (int nc = 0; nc < 4; ++nc) {
+            const int k = k0 + 16 * nc + j;
+            const bool kin = nc < nkb && k < a.K_c;
+#pragma unroll
+            for (int s = 0; s < MSX; ++s)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int m = 32 * s + 8 * g + 2 * q;
+                    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rw, kin ? (m * a.K_c + k) * 2 : kOut, 0, 0);
+                    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rw, kin ? ((m + 1) * a.K_c + k) * 2 : kOut, 0, 0);
+                    wt[nc][s][q] = lo | (hi << 16);
+                }
+        }
+    }
+
+    f32x4_t accw[MR][4];
+#pragma unroll
+    for (int mr = 0; mr < MR; ++mr)
+#pragma unroll
+        for (int nc = 0; nc < 4; ++nc) accw[mr][nc] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    // The wave's C rows of candidate e (rows past its blocks or past K_c read as zero).
+    u32x4_t cf[4][KS];
+    auto load_c = [&](int e) {
+        const bool ok = e < e1;
+        const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(ok ? a.C + (size_t)e * a.K_c * D : nullptr, ok ? cbytes : 0);
+#pragma unroll
+        for (int nc = 0; nc < 4; ++nc) {
+            const int off = nc < nkb ? (k0 + 16 * nc + j) * RB + 16 * g : kOut;
+#pragma unroll
+            for (int t = 0; t < KS; ++t)
+                cf[nc][t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * t, 0, 0));
+        }
+    };
+
+    // dW_c: A = dY rows 16 mr + j, columns 32 t + 8 g .. +7, from buffer buf.
+    auto dw = [&](int buf) {
+        const uint32_t base = lds_addr(lds + buf * BUF);
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            u32x4_t av[MR];
+            uint32_t pa[MR];
+#pragma unroll
+            for (int mr = 0; mr < MR; ++mr) {
+                const int r = 16 * mr + j;
+                pa[mr] = base + (uint32_t)(r * RB + 16 * ((4 * t + g) ^ cand_sw<D>(r)));
+            }
+            lds_read_n<MR>(av, pa);
+#pragma unroll
+            for (int nc = 0; nc < 4; ++nc) {
+                if (nc >= nkb) continue;
+#pragma unroll
+                for (int mr = 0; mr < MR; ++mr)
+                    if (mr < nmr) accw[mr][nc] = mfma_bf16(av[mr], cf[nc][t], accw[mr][nc]);
+            }
+        }
+    };
+
+    // dC[e] rows k0 .. k0 + 16*4 - 1 (the wave's blocks), from buffer buf.  The 128-column group
+    // goes in two halves h: 8-byte reads of columns 8j + 4h .. +3, so MFMA t yields column
+    // 8j + 4h + t and a lane stores 8 contiguous bytes per row.
+    auto dcp = [&](int e, int buf) {
+        const uint32_t base = lds_addr(lds + buf * BUF);
+        const bool ok = e < e1;
+        const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(ok ? a.dC + (size_t)e * a.K_c * D : nullptr, ok ? cbytes : 0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f32x4_t acc[4][4];
+#pragma unroll
+            for (int nc = 0; nc < 4; ++nc)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc[nc][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < MSX; ++s) {
+                if (s >= ms) break;
+                u32x2_t rv[8];
+                uint32_t pr[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int row = 32 * s + 8 * g + r;
+                    pr[r] = base + (uint32_t)(row * RB + 16 * (j ^ cand_sw<D>(row)) + 8 * h);
+                }
+                lds_read_b64x8(rv, pr);
+                RowBits<4> raw[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) raw[r].v = rv[r];
+                u32x4_t b[4];
+                transpose_rows<4>(raw, b);
+#pragma unroll
+                for (int nc = 0; nc < 4; ++nc) {
+                    if (nc >= nkb) continue;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) acc[nc][t] = mfma_bf16(wt[nc][s], b[t], acc[nc][t]);
+                }
+            }
+#pragma unroll
+            for (int nc = 0; nc < 4; ++nc)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int k = k0 + 16 * nc + 4 * g + i;
+                    const u32x2_t w = {pack_bf16x2(acc[nc][0][i], acc[nc][1][i]), pack_bf16x2(acc[nc][2][i], acc[nc][3][i])};
+                    __builtin_amdgcn_raw_buffer_store_b64(w, rs, nc < nkb ? (k * D + 8 * j + 4 * h) * 2 : kOut, 0, kDcStore);
+                }
+        }
+        if constexpr (W2 == 2) {
+            f32x4_t acc[4][2];
+#pragma unroll
+            for (int nc = 0; nc < 4; ++nc) acc[nc][0] = acc[nc][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < MSX; ++s) {
+                if (s >= ms) break;
+                uint32_t rv[8], pr[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int row = 32 * s + 8 * g + r;
+                    pr[r] = base + (uint32_t)(row * RB + 16 * ((16 + (j >> 2)) ^ cand_sw<D>(row)) + 4 * (j & 3));
+                }
+                lds_read_b32x8(rv, pr);
+                RowBits<2> raw[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) raw[r].v = rv[r];
+                u32x4_t b[2];
+                transpose_rows<2>(raw, b);
+#pragma unroll
+                for (int nc = 0; nc < 4; ++nc) {
+                    if (nc >= nkb) continue;
+                    acc[nc][0] = mfma_bf16(wt[nc][s], b[0], acc[nc][0]);
+                    acc[nc][1] = mfma_bf16(wt[nc][s], b[1], acc[nc][1]);
+                }
+            }
+#pragma unroll
+            for (int nc = 0; nc < 4; ++nc)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int k = k0 + 16 * nc + 4 * g + i;
+                    __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(acc[nc][0][i], acc[nc][1][i]), rs,
+                                                          nc < nkb ? (k * D + 128 + 2 * j) * 2 : kOut, 0, kDcStore);
+                }
+        }
+    };
+
+    stage(e0, 0);
+    load_c(e0);
+    vm_wait<4 * KS>();            // the first copy has landed (the C loads were issued after it)
+    wg_barrier();
+    for (int e = e0; e < e1; ++e) {
+        const int buf = (e - e0) & 1;
+        stage(e + 1, buf ^ 1);   // past the chunk: an empty range (zeros into the idle buffer)
+        dw(buf);
+        if constexpr (EARLY_C) load_c(e + 1);
+        dcp(e, buf);
+        vm_wait<NST>();          // the next copy (and any C loads before the dC phase) landed
+        if constexpr (!EARLY_C) load_c(e + 1);
+        wg_barrier();            // every wave is done with buf and sees the next copy
+    }
+
+    float *out = a.part + (size_t)blockIdx.x * a.M * a.K_c;
+#pragma unroll
+    for (int mr = 0; mr < MR; ++mr)
+#pragma unroll
+        for (int nc = 0; nc < 4; ++nc) {
+            const int k = k0 + 16 * nc + j;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * mr + 4 * g + i;
+                if (nc < nkb && m < a.M && k < a.K_c) out[(size_t)m * a.K_c + k] = accw[mr][nc][i];
+            }
+        }
+}
+
 int grid_for(long long work, int per_block) {
     long long blocks = (work + per_block - 1) / per_block;
     if (blocks > 4096) blocks = 4096;
@@ -380,6 +668,29 @@ hipError_t launch_wgrad(const WgradArgs &a, hipStream_t s) {
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+bool bwd_cand_supported(int M, int K_c, int D) {
+    return (D == 128 || D == 160) && M >= 1 && M <= 128 && K_c >= 1 && K_c <= 256;
+}
+
+size_t bwd_cand_lds_bytes(int M, int D) {
+    const int mr = M <= 96 ? 6 : 8;
+    const int ni = (mr + 1) / 2 * 2 * D / 32;
+    return (size_t)2 * 4 * ((ni + 3) / 4) * 1024;
+}
+
+hipError_t launch_bwd_cand(const BwdCandArgs &a, hipStream_t s) {
+    if (!bwd_cand_supported(a.M, a.K_c, a.D) || a.n_chunks < 1) return hipErrorInvalidValue;
+    void (*k)(BwdCandArgs);
+    if (a.D == 160) k = a.M <= 96 ? bwd_cand_kernel<6, 2> : bwd_cand_kernel<8, 2>;
+    else k = a.M <= 96 ? bwd_cand_kernel<6, 0> : bwd_cand_kernel<8, 0>;
+    const size_t lds = bwd_cand_lds_bytes(a.M, a.D);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    BwdCandArgs args = a;
+    void *params[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void *>(k), dim3(a.n_chunks), dim3(256), params, lds, s);
 }
 
 hipError_t launch_wgrad_reduce(const WgradReduceArgs &a, hipStream_t s) {

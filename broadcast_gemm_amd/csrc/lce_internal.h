@@ -243,4 +243,18 @@ struct WgradReduceArgs {
 };
 hipError_t launch_wgrad_reduce(const WgradReduceArgs &a, hipStream_t s);
 
+// One pass over the candidates for dC and the dW_c partials: dC[b] = W_c^T . dY[b] and
+// part[c] = sum over the candidates b of chunk c of dY[b] . C[b]^T, with dY[b] read once.
+// Applies when D is 128 or 160, M <= 128 and K_c <= 256 (bwd_cand_supported).
+struct BwdCandArgs {
+    const uint16_t *dY, *C, *W_c;   // [B_c][M][D], [B_c][K_c][D], [M][K_c]
+    uint16_t *dC;                   // [B_c][K_c][D]
+    float *part;                    // [n_chunks][M][K_c]
+    int B_c, M, K_c, D;
+    int per_chunk, n_chunks;        // candidates per chunk (one block each), ceil(B_c / per_chunk)
+};
+bool bwd_cand_supported(int M, int K_c, int D);
+size_t bwd_cand_lds_bytes(int M, int D);
+hipError_t launch_bwd_cand(const BwdCandArgs &a, hipStream_t s);
+
 }  // namespace ikbo

@@ -190,3 +190,61 @@ def test_backward_edge_cases():
             fwd_only.backward(g, U, C, mp, W_u, W_c)
     finally:
         fwd_only.close()
+
+
+ONE_PASS = [
+    # (B_u, B_c, K_u, K_c, M, D, map): the one-pass dC + dW_c launch at its edges
+    (3, 300, 40, 13, 96, 160, "random"),      # one K_c block: three waves own none; 300 > 256 chunks
+    (2, 257, 33, 256, 128, 128, "sorted"),    # sixteen K_c blocks (four per wave); chunks of 2 and 1
+    (4, 9, 50, 49, 33, 160, "random"),        # M = 33: two 32-row steps, the second mostly zero rows
+    (1, 1, 20, 70, 1, 128, "sorted"),         # M = 1, one candidate
+    (5, 520, 64, 100, 112, 160, "sorted"),    # M = 112 on the 128-row kernel, ragged K_c
+]
+
+
+@pytest.mark.parametrize("shape", ONE_PASS, ids=[f"{s[0]}x{s[1]}-K{s[2]}_{s[3]}-M{s[4]}-D{s[5]}" for s in ONE_PASS])
+def test_backward_one_pass_elementwise(shape):
+    """dC and dW_c from the one-pass launch (dY read once for both) against the oracle,
+    element by element, at shapes on its edges."""
+    import oracle
+    B_u, B_c, K_u, K_c, M, D, kind = shape
+    log(f"[backward] one pass shape={shape}")
+    cfg = LceConfig("bwd1", B_u, B_c, K_u, K_c, M, D, "bf16", kind, 91)
+    x = make_inputs(cfg)
+    dY = make_upstream_grad(cfg)
+    plan = bga.LcePlan(B_u, B_c, K_u, K_c, M, D, dtype="bf16", flags=bga.FLAG_BACKWARD)
+    try:
+        assert plan.info()["bwd_cand_chunks"] > 0
+        out = plan.backward(to_dev(dY), to_dev(x.U), to_dev(x.C), to_dev(x.map), to_dev(x.W_u), to_dev(x.W_c))
+        st = plan.check()
+        assert st == bga.IKBO_OK, bga.status_str(st)
+        got = tuple(to_f64(t) for t in out)
+    finally:
+        plan.close()
+    ref = oracle.lce_backward_f64(dY, x.U, x.C, x.map, x.W_u, x.W_c)
+    for name, g, r in zip(("dU", "dC", "dW_u", "dW_c"), got, ref):
+        assert g.shape == r.shape, name
+        assert_close(g, r, f"{shape} {name}")
+
+
+def test_backward_separate_launches_still_match(monkeypatch):
+    """With the one-pass launch switched off (IKBO_BWD_FUSED=0, read when the plan is made),
+    dC and dW_c come from the row-tile engine and the weight-gradient kernel, as for shapes the
+    one-pass launch does not take; both routes meet the bar at the 70:1 dimensions."""
+    import oracle
+    monkeypatch.setenv("IKBO_BWD_FUSED", "0")
+    cfg = LceConfig("bwd0", 5, 70, 301, 197, 96, 160, "bf16", "sorted", 78)
+    log("[backward] separate launches")
+    x = make_inputs(cfg)
+    dY = make_upstream_grad(cfg)
+    plan = bga.LcePlan(cfg.B_u, cfg.B_c, cfg.K_u, cfg.K_c, cfg.M, cfg.D, dtype="bf16", flags=bga.FLAG_BACKWARD)
+    try:
+        assert plan.info()["bwd_cand_chunks"] == 0
+        out = plan.backward(to_dev(dY), to_dev(x.U), to_dev(x.C), to_dev(x.map), to_dev(x.W_u), to_dev(x.W_c))
+        assert plan.check() == bga.IKBO_OK
+        got = tuple(to_f64(t) for t in out)
+    finally:
+        plan.close()
+    ref = oracle.lce_backward_f64(dY, x.U, x.C, x.map, x.W_u, x.W_c)
+    for name, g, r in zip(("dU", "dC", "dW_u", "dW_c"), got, ref):
+        assert_close(g, r, f"separate {name}")
