@@ -69,6 +69,7 @@ struct ikbo_lce_plan_s {
     int seg_T, seg_slices;                // segment sums: most chunks, 512-element slices
     int wgc_chunks, wgu_chunks;           // most entry chunks of the dW_c and dW_u products
     int cand_chunks;                      // one-pass dC + dW_c: most chunks (0: separate launches)
+    int cand_always;                      // take it for every batch size (IKBO_BWD_FUSED=2)
     uint16_t *Wt_c, *W_dup, *S2;
     int32_t *perm, *su, *off;
     float *seg_part, *part_c, *part_u;
@@ -360,6 +361,7 @@ int ikbo_lce_plan(ikbo_lce_plan_t *out, int max_B_u, int max_B_c, int K_u, int K
                                  env_int("IKBO_BWD_FUSED", 1) != 0
                              ? std::max(1, std::min(p->n_cu, std::max(max_B_c, 1)))
                              : 0;
+        p->cand_always = env_int("IKBO_BWD_FUSED", 1) == 2 ? 1 : 0;
         if (p->dc_bpc < 1 || (long long)p->dc_mpad * D * 4 >= (1LL << 31) ||
             bwd_prep_lds_bytes(max_B_u, max_B_c) > (size_t)std::min(max_lds, 64 * 1024)) {
             delete p;
@@ -882,12 +884,15 @@ int ikbo_lce_backward(ikbo_lce_plan_t p, const void *dY, const void *U, const vo
     // The one-pass launch (dC and the dW_c partials) holds every CU, so the other launches gain
     // nothing from running beside it and it runs on the caller's stream; the cross-stream events
     // would only add their own latency.
-    // It is taken when each CU's chunk is short (at most 8 candidates: the separate launches'
-    // fixed costs dominate there) or when the K_c row blocks deal out evenly over the four waves
-    // (otherwise the wave with one block more sets the pace of every candidate): measured, at
-    // 4096 candidates and K_c = 197 the separate launches were faster (233 against 259 us).
+    // It moves about as many bytes as the separate launches (dC's writes and C's reads dominate;
+    // it saves dY's second read but writes one dW_c partial per CU), so it pays where the separate
+    // launches carry fixed costs of their own.  Taken where it measured faster (bench, rotated
+    // buffers, same GPU): chunks of at most 2 candidates (10:1, 256 candidates: 59.7 against
+    // 82-86 us) and M above 96 (10000:1, M = 128: 953 against 1481 us); not at 70:1 (4 per CU:
+    // 91.7 against 87.4 us) or at 4096 random candidates (16 per CU: 287 against 263 us).
+    // IKBO_BWD_FUSED=2 takes it always, 0 never.
     const bool one_pass = p->cand_chunks > 0 && B_c > 0 &&
-                          (ceil_div(B_c, p->n_cu) <= 8 || ceil_div(K_c, 16) % 4 == 0);
+                          (p->cand_always || ceil_div(B_c, p->n_cu) <= 2 || M > 96);
     const bool fork = env_int("IKBO_BWD_STREAMS", one_pass ? 0 : 1) != 0;
     hipStream_t s_dc = s, s_du = s;
     int joined = 0;

@@ -412,6 +412,11 @@ __global__ void __launch_bounds__(256) bwd_cand_kernel(BwdCandArgs a) {
     const int n_kb = (a.K_c + 15) / 16;
     const int nkb = n_kb / 4 + (wv < n_kb % 4 ? 1 : 0);
     const int k0 = 16 * (wv * (n_kb / 4) + imin_t(wv, n_kb % 4));
+    // For dW_c a wave takes the blocks that wave 3 - wv takes for dC, so that a wave with one
+    // dC block more has one dW_c block fewer when the blocks do not deal out evenly.
+    const int wr = 3 - wv;
+    const int nkbw = n_kb / 4 + (wr < n_kb % 4 ? 1 : 0);
+    const int kw0 = 16 * (wr * (n_kb / 4) + imin_t(wr, n_kb % 4));
     const int cbytes = a.K_c * RB;                // one C[b] or dC[b] matrix
     constexpr int kOut = 1 << 30;                 // an offset past every range: reads 0, writes dropped
 
@@ -462,14 +467,14 @@ __global__ void __launch_bounds__(256) bwd_cand_kernel(BwdCandArgs a) {
 #pragma unroll
         for (int nc = 0; nc < 4; ++nc) accw[mr][nc] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    // The wave's C rows of candidate e (rows past its blocks or past K_c read as zero).
+    // The wave's C rows of candidate e for dW_c (rows past its blocks or past K_c read as zero).
     u32x4_t cf[4][KS];
     auto load_c = [&](int e) {
         const bool ok = e < e1;
         const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(ok ? a.C + (size_t)e * a.K_c * D : nullptr, ok ? cbytes : 0);
 #pragma unroll
         for (int nc = 0; nc < 4; ++nc) {
-            const int off = nc < nkb ? (k0 + 16 * nc + j) * RB + 16 * g : kOut;
+            const int off = nc < nkbw ? (kw0 + 16 * nc + j) * RB + 16 * g : kOut;
 #pragma unroll
             for (int t = 0; t < KS; ++t)
                 cf[nc][t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * t, 0, 0));
@@ -491,7 +496,7 @@ __global__ void __launch_bounds__(256) bwd_cand_kernel(BwdCandArgs a) {
             lds_read_n<MR>(av, pa);
 #pragma unroll
             for (int nc = 0; nc < 4; ++nc) {
-                if (nc >= nkb) continue;
+                if (nc >= nkbw) continue;
 #pragma unroll
                 for (int mr = 0; mr < MR; ++mr)
                     if (mr < nmr) accw[mr][nc] = mfma_bf16(av[mr], cf[nc][t], accw[mr][nc]);
@@ -602,11 +607,11 @@ __global__ void __launch_bounds__(256) bwd_cand_kernel(BwdCandArgs a) {
     for (int mr = 0; mr < MR; ++mr)
 #pragma unroll
         for (int nc = 0; nc < 4; ++nc) {
-            const int k = k0 + 16 * nc + j;
+            const int k = kw0 + 16 * nc + j;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 16 * mr + 4 * g + i;
-                if (nc < nkb && m < a.M && k < a.K_c) out[(size_t)m * a.K_c + k] = accw[mr][nc][i];
+                if (nc < nkbw && m < a.M && k < a.K_c) out[(size_t)m * a.K_c + k] = accw[mr][nc][i];
             }
         }
 }

@@ -27,11 +27,14 @@ LINES = [
     "constexpr int BUF = 4 * NQ * 1024;",
     "const int nkb = n_kb / 4 + (wv < n_kb % 4 ? 1 : 0);",
     "const int k0 = 16 * (wv * (n_kb / 4) + imin_t(wv, n_kb % 4));",
+    "const int wr = 3 - wv;",
+    "const int nkbw = n_kb / 4 + (wr < n_kb % 4 ? 1 : 0);",
+    "const int kw0 = 16 * (wr * (n_kb / 4) + imin_t(wr, n_kb % 4));",
     "const int q = wv + 4 * i;",
     "const int P = 64 * q + lane;",
     "const int r = P / CH, c = (P % CH) ^ cand_sw<D>(r);",
     "q < NI ? r * RB + 16 * c : kOut, 0, 0, 0);",
-    "const int off = nc < nkb ? (k0 + 16 * nc + j) * RB + 16 * g : kOut;",
+    "const int off = nc < nkbw ? (kw0 + 16 * nc + j) * RB + 16 * g : kOut;",
     "cf[nc][t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * t, 0, 0));",
     "pa[mr] = base + (uint32_t)(r * RB + 16 * ((4 * t + g) ^ cand_sw<D>(r)));",
     "pr[r] = base + (uint32_t)(row * RB + 16 * (j ^ cand_sw<D>(row)) + 8 * h);",
@@ -142,6 +145,18 @@ def test_k_blocks_dealt_once(K_c):
                             o = (kk * D + 128 + 2 * j) * 2
                             assert (o + 4 <= K_c * RB) if kk < K_c else (o >= K_c * RB)
     assert sorted(blocks) == list(range(n_kb))
+    # dW_c: wave wv takes wave (3 - wv)'s dC blocks; every block once, and no wave holds more
+    # than one block above the average over both products
+    wblocks, load = [], []
+    for wv in range(4):
+        wr = 3 - wv
+        nkbw = n_kb // 4 + (1 if wr < n_kb % 4 else 0)
+        kw0 = 16 * (wr * (n_kb // 4) + min(wr, n_kb % 4))
+        assert nkbw <= 4
+        wblocks += [kw0 // 16 + nc for nc in range(nkbw)]
+        load.append(n_kb // 4 + (1 if wv < n_kb % 4 else 0) + nkbw)
+    assert sorted(wblocks) == list(range(n_kb))
+    assert max(load) - min(load) <= 1
 
 
 @pytest.mark.parametrize("M,D", SHAPES)
