@@ -331,13 +331,16 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
     uint16_t *wl_c = lds;
     uint16_t *wl_u = lds + (a.n_cand > 0 && !shared ? lds_w_elems(a.M, a.K_wc) : 0);
     const bool need_u = bid * wpb < a.n_user;   // this block holds user units
+    // A block of user waves only gets no candidate unit when the candidates make a single round
+    // (round 0 skips the user waves, and there is no tail): it needs no W_c.
+    const bool user_only = (bid + 1) * wpb <= nuw && a.n_cand <= V;
     // Batches: 15 blocks of 16 bytes per thread cover W_u of 96 x 301 and 10 cover W_c of
     // 96 x 197; with the opening steps that makes at most 63 loads per wave in flight.
     T.prologue_first(rs);
     auto rest = [&]() { T.prologue_rest(rs); };
     if (need_u) {
         stage_flat<15>(a.W_u, a.M * a.K_u, wl_u, rest);
-        if (a.n_cand > 0 && !shared) stage_flat<10>(a.W_c, a.M * a.K_wc, wl_c, [] {});
+        if (a.n_cand > 0 && !shared && !user_only) stage_flat<10>(a.W_c, a.M * a.K_wc, wl_c, [] {});
     }
     else if (a.n_cand > 0)
         stage_flat<10>(a.W_c, a.M * a.K_wc, wl_c, rest);
@@ -367,7 +370,7 @@ __global__ void __launch_bounds__(kRowsBlock, 1) lce_rows_kernel(RowArgs a) {
         t = tn;
         rs = rs_next;
     }
-    if (need_u && shared) {
+    if (need_u && shared && !user_only) {
         // W_c replaces W_u once every wave of the block is done with it; the ring already
         // holds the first candidate unit's opening steps.
         __syncthreads();

@@ -39,6 +39,9 @@ ROWS_LINES = [
     "const int c = w >= nuw ? (k == 0 ? wr : V + (k - 1) * n_waves + wr) : V + k * n_waves + wr;",
     "for (int sidx = wr; sidx < n_sub;) {",
     "if (a.partner_sync && !need_u && a.n_cand >= V) __syncthreads();",
+    "const bool user_only = (bid + 1) * wpb <= nuw && a.n_cand <= V;",
+    "if (a.n_cand > 0 && !shared && !user_only) stage_flat<10>(a.W_c, a.M * a.K_wc, wl_c, [] {});",
+    "if (need_u && shared && !user_only) {",
 ]
 
 
@@ -100,6 +103,11 @@ def test_rows_schedule_covers_every_unit_once(case):
             assert len(u) <= 1 and (not u or u[0] == w)        # a user unit is a wave's first unit
             if cs and cs[0] < V:
                 assert w >= nuw                                  # round 0 skips the user waves
+    if n_cand <= V:                              # blocks of user waves only stage no W_c: no units
+        for b in range(n_waves // wpb):
+            if (b + 1) * wpb <= nuw:
+                for w in range(b * wpb, (b + 1) * wpb):
+                    assert not sched[w][1] and not sched[w][2], (b, w)
 
 
 @pytest.mark.parametrize("case", ROWS_CASES[::5])
