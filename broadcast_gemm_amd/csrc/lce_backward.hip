@@ -375,14 +375,15 @@ __device__ __forceinline__ void lds_read_b64x8(u32x2_t (&v)[8], const uint32_t (
 // Linear Compression": the candidate side of the product, differentiated).  For each candidate
 // b the block copies dY[b] ([M][D] bf16) into LDS once, by direct-to-LDS loads, double-buffered
 // (the next candidate's copy is in flight while this one is used).  Wave w owns up to four
-// 16-row blocks of K_c (the ceil(K_c/16) blocks dealt out over the four waves) in both products:
+// 16-row blocks of K_c for dC (the ceil(K_c/16) blocks dealt out over the four waves) and the
+// blocks of wave 3 - w for dW_c:
 //   dW_c: acc[m][k] += sum_d dY[b][m][d] C[b][k][d]  (A: dY rows from LDS; B: the wave's C rows
 //         from memory, one 16-byte load per fragment; the accumulators stay in registers for the
 //         whole chunk and are written once, as the chunk's partial);
 //   dC:   dC[b][k][d] = sum_m W_c[m][k] dY[b][m][d]  (A: the wave's rows of W_c^T, gathered into
 //         registers once; B: dY from LDS in the row tile's column layout, lane slot j taking 8
-//         rows of columns 8j..8j+7, and of 128+2j, 128+2j+1 at D = 160, transposed in registers,
-//         so that a lane's outputs are runs of consecutive columns of dC).
+//         rows of columns 8j + 4h .. +3 in half h, and of 128+2j, 128+2j+1 at D = 160,
+//         transposed in registers, so that a lane's outputs are runs of consecutive columns).
 // Rows of the copy from M up to the next multiple of 32 read as zero (its source range ends at
 // M rows), and so do W_c^T elements past M or K_c.  Every memory operation of an iteration is
 // issued unconditionally (absent rows and candidates go through empty or out-of-range buffer
