@@ -248,3 +248,23 @@ def test_backward_separate_launches_still_match(monkeypatch):
     ref = oracle.lce_backward_f64(dY, x.U, x.C, x.map, x.W_u, x.W_c)
     for name, g, r in zip(("dU", "dC", "dW_u", "dW_c"), got, ref):
         assert_close(g, r, f"separate {name}")
+
+
+def test_backward_one_pass_forced_long_chunks(monkeypatch):
+    """The one-pass launch forced (IKBO_BWD_FUSED=2) on the 4096-candidate random-map workload,
+    where the plan would not take it: chunks of 16 candidates per CU, sampled rows and weight
+    elements against the oracle."""
+    import oracle
+    monkeypatch.setenv("IKBO_BWD_FUSED", "2")
+    cfg = CONFIG_BY_NAME["large-unsorted"]
+    log("[backward] one pass forced, large-unsorted")
+    x = make_inputs(cfg)
+    dY = make_upstream_grad(cfg)
+    dU, dC, dW_u, dW_c = gpu_backward(x, dY)
+    dc, du, dw = _samples(cfg, x.map, np.random.default_rng(47))
+    oc, ou, ow = oracle.lce_backward_rows_f64(dY, x.U, x.C, x.map, x.W_u, x.W_c, dc, du, dw)
+    assert_close(np.stack([dC[b, k] for b, k in dc]), oc, "forced one pass dC rows")
+    assert_close(np.stack([dU[u, k] for u, k in du]), ou, "forced one pass dU rows")
+    K_u = cfg.K_u
+    gw = np.array([dW_u[m, k] if k < K_u else dW_c[m, k - K_u] for m, k in dw])
+    assert_close(gw, ow, "forced one pass dW elements")
